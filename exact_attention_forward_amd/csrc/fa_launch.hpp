@@ -1,0 +1,101 @@
+// Kernel instantiation and launch helpers shared by the per-dtype translation
+// units.  Tile shapes per (input type, head dim) live in TileCfg.
+#pragma once
+#include "fa_bwd.hpp"
+#include "fa_fwd.hpp"
+
+namespace fa {
+
+// NW waves per workgroup; MR 16-row subtiles per wave; BC/BQ rows of the
+// streamed side per LDS block.
+template <typename TIn, int HD>
+struct TileCfg;
+
+template <int HD>
+struct TileCfg<float, HD> {
+  static constexpr int FWD_NW = 4, FWD_MR = 2, FWD_BC = 32;
+  static constexpr int DQ_NW = 4, DQ_MR = 2, DQ_BC = 32;
+  static constexpr int DKV_NW = 4, DKV_MR = 2, DKV_BQ = 32;
+};
+template <>
+struct TileCfg<bf16_t, 64> {
+  static constexpr int FWD_NW = 4, FWD_MR = 2, FWD_BC = 64;
+  static constexpr int DQ_NW = 4, DQ_MR = 2, DQ_BC = 64;
+  static constexpr int DKV_NW = 4, DKV_MR = 2, DKV_BQ = 64;
+};
+template <>
+struct TileCfg<bf16_t, 128> {
+  static constexpr int FWD_NW = 4, FWD_MR = 2, FWD_BC = 64;
+  static constexpr int DQ_NW = 4, DQ_MR = 1, DQ_BC = 64;
+  static constexpr int DKV_NW = 4, DKV_MR = 1, DKV_BQ = 64;
+};
+
+inline int launch_status() { return hipGetLastError() == hipSuccess ? 0 : -5; }
+
+template <typename TIn, int HD, bool CAUSAL, int PREC>
+int run_fwd(const FwdArgs& a, hipStream_t s) {
+  using C = TileCfg<TIn, HD>;
+  constexpr int BR = C::FWD_NW * 16 * C::FWD_MR;
+  const long nqt = (a.T + BR - 1) / BR;
+  const long grid = nqt * a.B * a.H;
+  hipLaunchKernelGGL((fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC>), dim3((unsigned)grid),
+                     dim3(C::FWD_NW * 64), 0, s, a);
+  return launch_status();
+}
+
+template <typename TIn, int HD>
+int run_delta(const BwdArgs& a, hipStream_t s) {
+  constexpr int RPB = 256 / (HD / 4);
+  const long nrows = (long)a.B * a.T * a.H;
+  hipLaunchKernelGGL((delta_kernel<TIn, HD>), dim3((unsigned)((nrows + RPB - 1) / RPB)), dim3(256), 0, s, a);
+  return launch_status();
+}
+
+template <typename TIn, int HD, bool CAUSAL, int PREC>
+int run_dq(const BwdArgs& a, hipStream_t s) {
+  using C = TileCfg<TIn, HD>;
+  constexpr int BR = C::DQ_NW * 16 * C::DQ_MR;
+  const long grid = (long)((a.T + BR - 1) / BR) * a.B * a.H;
+  hipLaunchKernelGGL((dq_kernel<TIn, HD, CAUSAL, PREC, C::DQ_NW, C::DQ_MR, C::DQ_BC>), dim3((unsigned)grid),
+                     dim3(C::DQ_NW * 64), 0, s, a);
+  return launch_status();
+}
+
+template <typename TIn, int HD, bool CAUSAL, int PREC>
+int run_dkv(const BwdArgs& a, hipStream_t s) {
+  using C = TileCfg<TIn, HD>;
+  constexpr int BK = C::DKV_NW * 16 * C::DKV_MR;
+  const long grid = (long)((a.T + BK - 1) / BK) * a.B * a.H;
+  hipLaunchKernelGGL((dkv_kernel<TIn, HD, CAUSAL, PREC, C::DKV_NW, C::DKV_MR, C::DKV_BQ>), dim3((unsigned)grid),
+                     dim3(C::DKV_NW * 64), 0, s, a);
+  return launch_status();
+}
+
+enum Stage { kFwd = 0, kDq = 1, kDkv = 2 };
+
+template <typename TIn, int HD, bool CAUSAL, int PREC>
+int run_stage(int stage, const void* args, hipStream_t s) {
+  switch (stage) {
+    case kFwd: return run_fwd<TIn, HD, CAUSAL, PREC>(*static_cast<const FwdArgs*>(args), s);
+    case kDq: return run_dq<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);
+    default: return run_dkv<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);
+  }
+}
+
+template <typename TIn, int HD>
+int run_stage_hd(int stage, const void* args, bool causal, int prec, hipStream_t s) {
+  if constexpr (sizeof(TIn) == 2) {
+    if (prec == 1)
+      return causal ? run_stage<TIn, HD, true, 1>(stage, args, s) : run_stage<TIn, HD, false, 1>(stage, args, s);
+  }
+  return causal ? run_stage<TIn, HD, true, 0>(stage, args, s) : run_stage<TIn, HD, false, 0>(stage, args, s);
+}
+
+// Entry points of the per-dtype translation units.  prec: 0 single bf16
+// operand, 1 split operand.  Return 0, -3 (head dim not built) or -5.
+int stage_f32(int stage, int hd, const void* args, bool causal, hipStream_t s);
+int stage_bf16(int stage, int hd, const void* args, bool causal, int prec, hipStream_t s);
+int delta_f32(int hd, const BwdArgs& a, hipStream_t s);
+int delta_bf16(int hd, const BwdArgs& a, hipStream_t s);
+
+}  // namespace fa

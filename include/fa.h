@@ -1,0 +1,131 @@
+/*
+ * fa.h -- C ABI of the exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention with an online
+ * softmax (forward) and its gradient with recomputation (backward), as
+ * described in "Flash Attention 2 -- forward pass notes" (section "The
+ * algorithm" and "Loop (per (b, h, Q-tile))") and "Flash Attention 2 --
+ * backward pass notes" (section "The math (FA2 backward with recompute)").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.   q, k, v, dO, o, dq, dk, dv are dense row-major [B, T, H, hd]
+ *           tensors (the [B, T, C] activations with C = H * hd of the forward
+ *           notes).  lse and delta are dense [B, H, T] float32 vectors.
+ * Dtypes.   Inputs q, k, v, dO are FA_F32 (float32) or FA_BF16 (bfloat16
+ *           bits).  Every output and workspace is float32.
+ * Mask.     causal != 0 keeps key j for query i iff j <= i (diagonal kept);
+ *           causal == 0 keeps every key.  Self-attention only (one T).
+ * Scale.    Scores are scale * <q_i, k_j>; scale must be finite and > 0
+ *           (1/sqrt(hd) in the usual case).
+ * Memory.   Every pointer is a device pointer allocated by the caller,
+ *           16-byte aligned.  The library never allocates, frees or
+ *           synchronises; it only enqueues kernels on `stream` (a hipStream_t,
+ *           NULL for the default stream), in order, and returns.  Inputs are
+ *           read-only.  Outputs are fully overwritten (no pre-zeroing, nothing
+ *           accumulates).  Outputs must not overlap each other or any input.
+ * Errors.   0 on success, a negative FA_ERR_* code otherwise.  All argument
+ *           checks happen before the first launch, so a failing call writes
+ *           nothing.  A launch failure reports FA_ERR_LAUNCH; kernels already
+ *           enqueued by that call may have run.
+ * Sizes.    B, H, T >= 1; B * H * T * hd < 2^40 elements.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * Operand precision of the two products whose left factor is computed inside
+ * the kernel (P in P.V and dV, dS in dQ and dK).  Only meaningful for FA_BF16
+ * inputs; FA_F32 inputs accept FA_PREC_DEFAULT only and compute every product
+ * in float32.
+ *   FA_PREC_DEFAULT  same as FA_PREC_BF16 for bfloat16 inputs
+ *   FA_PREC_BF16     P and dS rounded to bfloat16 before the matrix product
+ *   FA_PREC_BF16X2   P and dS split into a bfloat16 value and a bfloat16
+ *                    residual, two products (about 16 significant bits)
+ * Accumulation is float32 in every mode.
+ */
+typedef enum { FA_PREC_DEFAULT = 0, FA_PREC_BF16 = 1, FA_PREC_BF16X2 = 2 } fa_precision;
+
+enum {
+  FA_OK = 0,
+  FA_ERR_ARG = -1,         /* null pointer, B/H/T < 1, bad scale/causal/enum, size overflow */
+  FA_ERR_ALIGN = -2,       /* a pointer is not 16-byte aligned */
+  FA_ERR_UNSUPPORTED = -3, /* (hd, dtype, precision) not built */
+  FA_ERR_ALIAS = -4,       /* an output overlaps an input or another output */
+  FA_ERR_LAUNCH = -5       /* the runtime rejected a kernel launch */
+};
+
+/*
+ * Forward pass: o = softmax(mask(scale * q k^T)) v per (batch, head), and
+ * lse[b, h, i] = m_i + ln(l_i), the natural-log log-sum-exp of row i's
+ * visible scores (forward notes, "Loop (per (b, h, Q-tile))" and "What's
+ * still needed for full FA2" item 1).  A row with no visible key would get
+ * o = 0 and lse = -inf; with T >= 1 every row sees key 0.
+ *   q, k, v   [B, T, H, hd] inputs of `dtype`
+ *   o         [B, T, H, hd] float32 output
+ *   lse       [B, H, T] float32 output
+ */
+int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T, int hd,
+               float scale, int causal, fa_dtype dtype, fa_precision prec, void* stream);
+
+/*
+ * Backward pass with recomputation (backward notes, "The math (FA2 backward
+ * with recompute)"): from the forward's o and lse and the upstream gradient
+ * dO = d loss / d o, writes dq, dk, dv.  Runs the three stages below in order
+ * on `stream`.
+ *   q, k, v, dO  [B, T, H, hd] inputs of `dtype`
+ *   o            [B, T, H, hd] float32, the forward output for these inputs
+ *   lse          [B, H, T] float32, the forward log-sum-exp
+ *   dq, dk, dv   [B, T, H, hd] float32 outputs
+ *   delta        [B, H, T] float32 caller-provided workspace; on return it
+ *                holds D_i = <dO_i, o_i>
+ */
+int fa_backward(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dO,
+                float* dq, float* dk, float* dv, float* delta, int B, int H, int T, int hd, float scale, int causal,
+                fa_dtype dtype, fa_precision prec, void* stream);
+
+/*
+ * The three backward stages, for callers that schedule them separately.
+ * fa_backward == fa_backward_delta; fa_backward_dq; fa_backward_dkv.
+ *
+ * fa_backward_delta: delta[b, h, i] = <dO[b, i, h, :], o[b, i, h, :]>, the
+ * pre-pass of the backward notes ("Why the WGSL kernel isn't shipped this
+ * turn", option 1).
+ */
+int fa_backward_delta(const float* o, const void* dO, float* delta, int B, int H, int T, int hd, fa_dtype dtype,
+                      void* stream);
+
+/*
+ * fa_backward_dq: one workgroup per query tile (backward notes, option 3,
+ * the dQ kernel); needs lse and delta.  Writes dq only.
+ */
+int fa_backward_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                   const float* delta, float* dq, int B, int H, int T, int hd, float scale, int causal,
+                   fa_dtype dtype, fa_precision prec, void* stream);
+
+/*
+ * fa_backward_dkv: one workgroup per key tile, walking every query that can
+ * see it (backward notes, option 3, the dK/dV kernel); needs lse and delta.
+ * Writes dk and dv only.
+ */
+int fa_backward_dkv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                    const float* delta, float* dk, float* dv, int B, int H, int T, int hd, float scale,
+                    int causal, fa_dtype dtype, fa_precision prec, void* stream);
+
+/* 1 if (hd, dtype) is built (f32: hd in {8,16,32,64,128}; bf16: {64,128}), else 0. */
+int fa_is_supported(int hd, fa_dtype dtype);
+
+/* Static string naming a status code; never NULL. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

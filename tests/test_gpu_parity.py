@@ -1,0 +1,168 @@
+"""GPU parity against the float64 oracle, through the C ABI (needs an MI355X).
+
+Small cases are compared element by element over every output; the
+full-size workloads are compared on sampled heads (every output element of
+those heads), with the same entry points and precision mode the bench times.
+Tolerances: max abs 2e-5 for float32 inputs, 2e-2 for bfloat16 inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_forward_amd as fa
+from exact_attention_forward_amd import inputs as I
+
+from gpu_util import BF16_TOL, F32_TOL, assert_within, full_errors, head_errors, run_case
+
+pytestmark = pytest.mark.gpu
+
+
+def show(case, prec, err):
+    print(f"[parity] {case.name} B{case.B} H{case.H} T{case.T} hd{case.hd} {case.dtype} causal={case.causal} "
+          f"prec={prec} " + " ".join(f"{k}={v:.2e}" for k, v in err.items()), flush=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_both_masks(causal):
+    c = I.tiny_case(causal)
+    err = full_errors(c, run_case(c))
+    show(c, 0, err)
+    assert_within(err, F32_TOL, c.name)
+
+
+@pytest.mark.parametrize("idx", range(len(I.RAGGED_SHAPES)))
+def test_ragged_causal(idx):
+    c = I.ragged_cases()[idx]
+    err = full_errors(c, run_case(c))
+    show(c, 0, err)
+    assert_within(err, F32_TOL, c.name)
+
+
+F32_EDGES = [(1, 1, 1, 64), (1, 2, 2, 8), (2, 1, 15, 16), (1, 3, 17, 32), (1, 1, 33, 128), (2, 2, 129, 64),
+             (1, 2, 300, 128), (1, 1, 513, 16)]
+
+
+@pytest.mark.parametrize("shape", F32_EDGES, ids=lambda s: "B{}H{}T{}hd{}".format(*s))
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_edges(shape, causal):
+    B, H, T, hd = shape
+    c = I.make_case(f"f32_edge", B, H, T, hd, I.F32, causal, 100 + T + hd)
+    err = full_errors(c, run_case(c))
+    show(c, 0, err)
+    assert_within(err, F32_TOL, c.name)
+
+
+BF16_EDGES = [(1, 1, 1, 64), (1, 2, 31, 64), (2, 1, 257, 64), (1, 2, 300, 128), (1, 1, 65, 128), (1, 1, 700, 64)]
+
+
+@pytest.mark.parametrize("shape", BF16_EDGES, ids=lambda s: "B{}H{}T{}hd{}".format(*s))
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("prec", [fa.FA_PREC_BF16, fa.FA_PREC_BF16X2])
+def test_bf16_edges(shape, causal, prec):
+    B, H, T, hd = shape
+    c = I.make_case("bf16_edge", B, H, T, hd, I.BF16, causal, 200 + T + hd)
+    err = full_errors(c, run_case(c, prec))
+    show(c, prec, err)
+    assert_within(err, BF16_TOL, c.name)
+    if prec == fa.FA_PREC_BF16X2:
+        # the split operand carries about 16 significant bits
+        assert_within(err, 1e-3, c.name + " split")
+
+
+def test_default_precision_is_bf16():
+    c = I.make_case("bf16_default", 1, 2, 200, 64, I.BF16, True, 7)
+    a, b = run_case(c, fa.FA_PREC_DEFAULT), run_case(c, fa.FA_PREC_BF16)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+# -- full-size workloads, sampled heads -------------------------------------------
+
+@pytest.fixture(scope="module")
+def gpt2m_f32():
+    return I.gpt2m_case(I.F32)
+
+
+@pytest.fixture(scope="module")
+def gpt2m_bf16():
+    return I.gpt2m_case(I.BF16)
+
+
+SAMPLE_HEADS = [(0, 0), (63, 15), (17, 5), (40, 11)]
+
+
+def check_sampled(case, prec, tol, heads):
+    out = run_case(case, prec)
+    for n, t in out.items():
+        assert bool(torch.isfinite(t).all()), f"{n} has unwritten or non-finite elements"
+    worst = {}
+    for b, h in heads:
+        for n, e in head_errors(case, out, b, h).items():
+            worst[n] = max(worst.get(n, 0.0), e)
+    show(case, prec, worst)
+    assert_within(worst, tol, case.name)
+    return out
+
+
+def test_gpt2m_f32_sampled(gpt2m_f32):
+    check_sampled(gpt2m_f32, fa.FA_PREC_DEFAULT, F32_TOL, SAMPLE_HEADS)
+
+
+def test_gpt2m_bf16_sampled(gpt2m_bf16):
+    check_sampled(gpt2m_bf16, fa.FA_PREC_BF16, BF16_TOL, SAMPLE_HEADS)
+
+
+def test_long_bf16_split_sampled():
+    c = I.long_case()
+    check_sampled(c, fa.FA_PREC_BF16X2, BF16_TOL, [(0, 0), (3, 15)])
+
+
+# -- properties --------------------------------------------------------------------
+
+def test_bitwise_deterministic(gpt2m_bf16):
+    c = I.make_case("det", 4, 4, 1024, 64, I.BF16, True, 8)
+    a, b = run_case(c), run_case(c)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("dtype,prec,tol", [(I.F32, 0, 1e-6), (I.BF16, fa.FA_PREC_BF16X2, 1e-5),
+                                             (I.BF16, fa.FA_PREC_BF16, 2.0 ** -8)])
+def test_constant_values_give_constant_output(dtype, prec, tol):
+    # V = 1 everywhere => O = 1 for every row, whatever the scores.  With P
+    # rounded to bfloat16 for the P.V product while the row sum l adds the
+    # unrounded weights, O = 1 holds to bfloat16 precision only.
+    c = I.make_case("ones", 2, 2, 333, 64, dtype, True, 9)
+    c.v = np.full_like(c.v, 0x3F80 if dtype == I.BF16 else 1.0)
+    out = run_case(c, prec)
+    assert float((out["O"] - 1).abs().max()) <= tol
+
+
+def test_stages_equal_combined_backward():
+    c = I.make_case("stages", 2, 3, 200, 64, I.BF16, True, 10)
+    ref = run_case(c)
+    from gpu_util import to_device
+    q, k, v, do = (to_device(c, n) for n in ("q", "k", "v", "do"))
+    B, T, H, hd = q.shape
+    dq, dk, dv = (torch.full_like(ref["dQ"], float("nan")) for _ in range(3))
+    delta = torch.full_like(ref["D"], float("nan"))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        fa.check(fa.fa_backward_delta(ref["O"], do, delta, B, H, T, hd, fa.FA_BF16, s))
+        fa.check(fa.fa_backward_dq(q, k, v, ref["L"], do, delta, dq, B, H, T, hd, c.scale, 1, fa.FA_BF16, 0, s))
+        fa.check(fa.fa_backward_dkv(q, k, v, ref["L"], do, delta, dk, dv, B, H, T, hd, c.scale, 1, fa.FA_BF16, 0, s))
+    torch.cuda.synchronize()
+    assert torch.equal(delta, ref["D"]) and torch.equal(dq, ref["dQ"])
+    assert torch.equal(dk, ref["dK"]) and torch.equal(dv, ref["dV"])
+
+
+def test_invalid_call_writes_nothing():
+    c = I.make_case("inval", 1, 1, 64, 64, I.F32, True, 11)
+    from gpu_util import to_device
+    q, k, v = (to_device(c, n) for n in ("q", "k", "v"))
+    o = torch.full((1, 64, 1, 64), 7.0, device="cuda")
+    lse = torch.full((1, 1, 64), 7.0, device="cuda")
+    assert fa.fa_forward(q, k, v, o, lse, 1, 1, 64, 64, -1.0, 1, fa.FA_F32, 0, None) == fa.FA_ERR_ARG
+    assert fa.fa_forward(q, k, v, o, q, 1, 1, 64, 64, 0.125, 1, fa.FA_F32, 0, None) == fa.FA_ERR_ALIAS
+    torch.cuda.synchronize()
+    assert bool((o == 7.0).all()) and bool((lse == 7.0).all())
