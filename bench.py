@@ -1,0 +1,218 @@
+"""Throughput of exact attention forward + backward on one MI355X.
+
+Workload: GPT-2-medium-shaped causal attention, B=64 H=16 T=1024 hd=64,
+bfloat16 inputs drawn N(0, 1) (seeded, synthetic), float32 accumulation and
+outputs, P and dS rounded to bfloat16 for their matrix products.
+
+One step = fa_forward, then the three backward stages (fa_backward_delta,
+fa_backward_dq, fa_backward_dkv -- exactly what fa_backward runs), with every
+input already resident in HBM.  W untimed warm-up steps, then K timed steps
+between two device synchronisations; HIP events on the launch stream time each
+kernel inside the timed region.
+
+The metric counts 14*hd flops per (query, visible key) pair, B*H*T^2/2 pairs
+for the causal mask.  The roofline object describes the kernel with the
+largest share of the step; its algorithmic flops are the products it must
+execute (forward 4*hd, dQ kernel 6*hd, dK/dV kernel 8*hd per pair).
+
+The CPU baseline times the float64 oracle on the host cores over a bounded
+sample of the same workload (whole heads), and compares those heads of the
+GPU outputs with it.
+
+``--counters`` runs a minimal program for rocprofv3 --pmc: a float32 copy of
+known size (the calibration kernel), then a few steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "attention fwd+bwd TFLOP/s (% MFMA peak), causal B64 H16 T1024 hd64, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+STAGES = ("fwd", "delta", "dq", "dkv")
+KERNEL_NAMES = {"fwd": "fwd_kernel", "delta": "delta_kernel", "dq": "dq_kernel", "dkv": "dkv_kernel"}
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "exact_attention_forward_amd" / "csrc").glob("*")):
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernels."""
+    p = ROOT / "profiles" / "traffic.json"
+    if not p.exists():
+        return None
+    rec = json.loads(p.read_text())
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(KERNEL_NAMES[stage])
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true", help="minimal run for rocprofv3 counter collection")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import exact_attention_forward_amd as fa
+    from exact_attention_forward_amd import inputs as I
+
+    case = I.gpt2m_case(I.BF16)
+    B, H, T, hd = case.B, case.H, case.T, case.hd
+    prec = fa.FA_PREC_BF16
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (up(getattr(case, n)) for n in ("q", "k", "v", "do"))
+    f32 = lambda *s: torch.empty(s, device=dev, dtype=torch.float32)
+    o, lse = f32(B, T, H, hd), f32(B, H, T)
+    dq, dk, dv, delta = f32(B, T, H, hd), f32(B, T, H, hd), f32(B, T, H, hd), f32(B, H, T)
+    stream = torch.cuda.current_stream(dev)
+    sc, dt = case.scale, fa.FA_BF16
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.check(fa.fa_forward(q, k, v, o, lse, B, H, T, hd, sc, 1, dt, prec, stream))
+        if ev is not None:
+            ev[1].record(stream)
+        fa.check(fa.fa_backward_delta(o, do, delta, B, H, T, hd, dt, stream))
+        if ev is not None:
+            ev[2].record(stream)
+        fa.check(fa.fa_backward_dq(q, k, v, lse, do, delta, dq, B, H, T, hd, sc, 1, dt, prec, stream))
+        if ev is not None:
+            ev[3].record(stream)
+        fa.check(fa.fa_backward_dkv(q, k, v, lse, do, delta, dk, dv, B, H, T, hd, sc, 1, dt, prec, stream))
+        if ev is not None:
+            ev[4].record(stream)
+
+    if args.counters:
+        x = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": "done", "copy_bytes": COPY_BYTES}), flush=True)
+        return 0
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    per = {s: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, s in enumerate(STAGES)}
+    pairs = B * H * T * T / 2
+    counted = 14 * hd * pairs
+    algo_flops = {"fwd": 4 * hd * pairs, "delta": 0.0, "dq": 6 * hd * pairs, "dkv": 8 * hd * pairs}
+    value = counted / (ms_step * 1e-3) / 1e12
+
+    dom = max(("fwd", "dq", "dkv"), key=lambda s: per[s])
+    achieved = algo_flops[dom] / (per[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom),
+                "kernel": KERNEL_NAMES[dom]}
+
+    kernels = {KERNEL_NAMES[s]: {"ms": round(per[s], 4),
+                                 "tflops": round(algo_flops[s] / (per[s] * 1e-3) / 1e12, 2) if algo_flops[s] else None}
+               for s in STAGES}
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16 inputs)",
+        "config": {"workload": "causal attention fwd+bwd B64 H16 T1024 hd64 bf16 (P, dS bf16 operands)",
+                   "B": B, "H": H, "T": T, "hd": hd, "causal": True, "precision": "FA_PREC_BF16"},
+        "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline, "kernels": kernels,
+        "device": torch.cuda.get_device_name(dev),
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(case, dict(O=o, L=lse, dQ=dq, dK=dk, dV=dv),
+                                                                 args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def cpu_baseline(case, out, budget_s: float):
+    """Time the float64 oracle on whole heads of the workload until the budget is spent."""
+    import numpy as np
+
+    from oracle import attention as oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    heads = [(b, h) for b in range(case.B) for h in range(case.H)]
+    order = np.random.default_rng(0).permutation(len(heads))
+    done, worst = [], {}
+    t0 = time.perf_counter()
+    for idx in order:
+        b, h = heads[idx]
+        qh, kh, vh, dh = (case.head_f64(n, b, h) for n in ("q", "k", "v", "do"))
+        O, L, _ = oracle.head_forward(qh, kh, vh, case.scale, case.causal)
+        dQ, dK, dV, _ = oracle.head_backward(qh, kh, vh, dh, case.scale, case.causal)
+        done.append((b, h))
+        for n, ref in (("O", O), ("L", L), ("dQ", dQ), ("dK", dK), ("dV", dV)):
+            g = out[n][b, h] if n == "L" else out[n][b, :, h]
+            worst[n] = max(worst.get(n, 0.0), float(np.abs(g.cpu().numpy().astype(np.float64) - ref).max()))
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = 14 * case.hd * case.T * case.T / 2 * len(done)
+    base = {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} of {case.B * case.H} heads (float64 NumPy, fwd+bwd per head), {el:.1f} s"}
+    parity = {"heads": len(done), "max_abs_err": {k: float(f"{v:.3e}") for k, v in worst.items()}, "tol": 2e-2,
+              "ok": all(v <= 2e-2 for v in worst.values())}
+    return base, parity
+
+
+if __name__ == "__main__":
+    sys.exit(main())
