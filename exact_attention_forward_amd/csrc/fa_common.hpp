@@ -21,6 +21,7 @@
 namespace fa {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -172,23 +173,26 @@ constexpr int lds_ld() {
 
 // Cooperative copy of rows [row0, row0 + ROWS) of a row-major global matrix
 // (leading dimension gld, nrows valid rows, HD columns) into registers, then
-// into an LDS tile.  Rows past nrows become zeros.
+// into an LDS tile.  Rows past nrows repeat row nrows - 1 (finite data, so a
+// zero weight on them contributes exactly zero); every kernel masks or zeroes
+// the weights of those rows.  The loads carry no branches.
 template <typename T, int HD, int ROWS, int NT>
 struct TileCopy {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int VPR = HD / VEC;  // vectors per row
   static constexpr int NV = ROWS * VPR;
   static constexpr int PER = (NV + NT - 1) / NT;
-  uint4 r[PER];
+  u32x4 r[PER];  // a native vector type, so the copies stay in registers
 
   __device__ __forceinline__ void load(const T* G, size_t gld, int row0, int nrows, int tid) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int v = tid + p * NT;
       const int row = v / VPR, col = (v % VPR) * VEC;
-      r[p] = make_uint4(0, 0, 0, 0);
-      if ((NV % NT == 0 || v < NV) && row0 + row < nrows)
-        r[p] = *reinterpret_cast<const uint4*>(G + (size_t)(row0 + row) * gld + col);
+      if (NV % NT == 0 || v < NV) {
+        const int gr = min(row0 + row, nrows - 1);
+        r[p] = *reinterpret_cast<const u32x4*>(G + (size_t)gr * gld + col);
+      }
     }
   }
   __device__ __forceinline__ void store(T* S, int ld, int tid) const {
@@ -196,7 +200,7 @@ struct TileCopy {
     for (int p = 0; p < PER; ++p) {
       const int v = tid + p * NT;
       const int row = v / VPR, col = (v % VPR) * VEC;
-      if (NV % NT == 0 || v < NV) *reinterpret_cast<uint4*>(S + row * ld + col) = r[p];
+      if (NV % NT == 0 || v < NV) *reinterpret_cast<u32x4*>(S + row * ld + col) = r[p];
     }
   }
 };

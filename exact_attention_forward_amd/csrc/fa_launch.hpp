@@ -2,7 +2,9 @@
 // units.  Tile shapes per (input type, head dim) live in TileCfg.
 #pragma once
 #include "fa_bwd.hpp"
+#include "fa_bwd32.hpp"
 #include "fa_fwd.hpp"
+#include "fa_fwd32.hpp"
 
 namespace fa {
 
@@ -10,6 +12,14 @@ namespace fa {
 // streamed side per LDS block.
 template <typename TIn, int HD>
 struct TileCfg;
+
+// bfloat16 kernels use 32x32 tiles: NW waves of 32 rows each.
+template <int HD>
+struct TileCfg32 {
+  static constexpr int FWD_NW = 4, FWD_BC = HD <= 64 ? 128 : 64;
+  static constexpr int DQ_NW = 4, DQ_BC = 64;
+  static constexpr int DKV_NW = 4, DKV_BQ = 64;
+};
 
 template <int HD>
 struct TileCfg<float, HD> {
@@ -34,6 +44,13 @@ inline int launch_status() { return hipGetLastError() == hipSuccess ? 0 : -5; }
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_fwd(const FwdArgs& a, hipStream_t s) {
+  if constexpr (sizeof(TIn) == 2) {
+    using C = TileCfg32<HD>;
+    const long grid = (long)((a.T + C::FWD_NW * 32 - 1) / (C::FWD_NW * 32)) * a.B * a.H;
+    hipLaunchKernelGGL((fwd32_kernel<HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC>), dim3((unsigned)grid),
+                       dim3(C::FWD_NW * 64), 0, s, a);
+    return launch_status();
+  }
   using C = TileCfg<TIn, HD>;
   constexpr int BR = C::FWD_NW * 16 * C::FWD_MR;
   const long nqt = (a.T + BR - 1) / BR;
@@ -53,6 +70,13 @@ int run_delta(const BwdArgs& a, hipStream_t s) {
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_dq(const BwdArgs& a, hipStream_t s) {
+  if constexpr (sizeof(TIn) == 2) {
+    using C = TileCfg32<HD>;
+    const long grid = (long)((a.T + C::DQ_NW * 32 - 1) / (C::DQ_NW * 32)) * a.B * a.H;
+    hipLaunchKernelGGL((dq32_kernel<HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC>), dim3((unsigned)grid),
+                       dim3(C::DQ_NW * 64), 0, s, a);
+    return launch_status();
+  }
   using C = TileCfg<TIn, HD>;
   constexpr int BR = C::DQ_NW * 16 * C::DQ_MR;
   const long grid = (long)((a.T + BR - 1) / BR) * a.B * a.H;
@@ -63,6 +87,13 @@ int run_dq(const BwdArgs& a, hipStream_t s) {
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_dkv(const BwdArgs& a, hipStream_t s) {
+  if constexpr (sizeof(TIn) == 2) {
+    using C = TileCfg32<HD>;
+    const long grid = (long)((a.T + C::DKV_NW * 32 - 1) / (C::DKV_NW * 32)) * a.B * a.H;
+    hipLaunchKernelGGL((dkv32_kernel<HD, CAUSAL, PREC, C::DKV_NW, C::DKV_BQ>), dim3((unsigned)grid),
+                       dim3(C::DKV_NW * 64), 0, s, a);
+    return launch_status();
+  }
   using C = TileCfg<TIn, HD>;
   constexpr int BK = C::DKV_NW * 16 * C::DKV_MR;
   const long grid = (long)((a.T + BK - 1) / BK) * a.B * a.H;
