@@ -34,9 +34,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, verbose: bool) -> Path:
-    out = OBJ / (Path(src).stem + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, "-c", str(CSRC / src), "-o", str(out)]
+def _compile(src: str, verbose: bool, defines=(), obj_dir: Path = OBJ) -> Path:
+    out = obj_dir / (Path(src).stem + ".o")
+    cmd = [hipcc(), *HIP_FLAGS, *[f"-D{d}" for d in defines], "-c", str(CSRC / src), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -46,17 +46,20 @@ def _compile(src: str, verbose: bool) -> Path:
     return out
 
 
-def build(verbose: bool = False) -> Path:
-    OBJ.mkdir(exist_ok=True)
+def build(verbose: bool = False, defines=(), out: Path = LIB) -> Path:
+    """Compile and link libfa.so.  `defines` (NAME=VALUE strings) override compile-time tile sizes."""
+    obj_dir = OBJ if not defines else OBJ / ("v_" + "_".join(d.replace("=", "") for d in defines))
+    obj_dir.mkdir(parents=True, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB.with_suffix(".so.tmp")
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, obj_dir), SOURCES))
+    LIB_OUT = Path(out)
+    tmp = LIB_OUT.with_suffix(".so.tmp")
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *map(str, objs), "-o", str(tmp)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, LIB_OUT)
+    return LIB_OUT
 
 
 if __name__ == "__main__":

@@ -8,11 +8,9 @@
 //  * S^T = K Q^T per 32-key tile: K from the LDS block, Q^T from registers.
 //  * O^T += V^T P^T: P^T straight from the S^T registers (see fa_mfma32.hpp),
 //    V^T by LDS transpose reads of the row-major V block.
-//  * Blocks wholly below the causal diagonal (and inside T) take a path with
-//    no masking and no per-tile branches, so the independent MFMA chains of
-//    the block interleave.  Blocks crossing the diagonal or the end of the
-//    sequence take a masked path that also skips 32-key tiles wholly above a
-//    wave's rows.
+//  * Every block runs straight-line code, so the independent MFMA chains of
+//    the block interleave; blocks crossing the causal diagonal or the end of
+//    the sequence add an element-wise mask before the row max.
 //  * The rescale of O by alpha is skipped when no row of the wave raised its
 //    running max in the block.
 #pragma once
@@ -82,20 +80,16 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void fwd32_kernel(FwdArg
 
   auto block = [&](const bf16_t* cK, const bf16_t* cV, const int j0, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
-    // A 32-key tile is live unless (masked path, causal) it lies wholly above the wave's rows.
-    auto live = [&](int kt) { return !(MASK && CAUSAL) || (j0 + 32 * kt <= r0 + 31); };
     f32x16 s[NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) s[kt] = zero16();
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-        if (live(kt)) s[kt] = mma32(ld_row32(cK, LD, 32 * kt, 16 * ks, n, h), qf[ks], s[kt]);
+      for (int kt = 0; kt < NKT; ++kt) s[kt] = mma32(ld_row32(cK, LD, 32 * kt, 16 * ks, n, h), qf[ks], s[kt]);
     if (MASK) {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
-        if (!live(kt)) continue;
         const int lim = vis - (j0 + 32 * kt);
 #pragma unroll
         for (int e = 0; e < 16; ++e)
@@ -105,27 +99,29 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void fwd32_kernel(FwdArg
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
-      if (live(kt)) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(mrow, mx * c2);
     const float muse = (mnew == -INFINITY) ? 0.f : mnew;
     const bool grew = mnew > mrow;
     const float alpha = (mrow == -INFINITY) ? 0.f : fast_exp2(mrow - mnew);
     mrow = mnew;
+    // P = exp2(s c2 - m); the row sum adds the unrounded float weights.
+    bf16x8 pk[NKT][2];
     float ls = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-      if (live(kt)) {
+    for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(fmaf(s[kt][e], c2, -muse));
-          s[kt][e] = p;
-          ls += p;
-        }
+      for (int e = 0; e < 16; ++e) {
+        s[kt][e] = fast_exp2(fmaf(s[kt][e], c2, -muse));
+        ls += s[kt][e];
       }
+      if (PREC == 0) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) pk[kt][st] = pack32(s[kt], st);
+      }
+    }
     lrow = lrow * alpha + ls;
     if (__any(grew)) {
 #pragma unroll
@@ -133,18 +129,16 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void fwd32_kernel(FwdArg
     }
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
-      if (live(kt)) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16x8 bf = pack32(s[kt], st);
-          bf16x8 bl;
-          if (PREC == 1) bl = pack32_lo(s[kt], st);
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 bf = PREC == 0 ? pk[kt][st] : pack32(s[kt], st);
+        bf16x8 bl;
+        if (PREC == 1) bl = pack32_lo(s[kt], st);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8 af = ld_tr32(cV, LD, 32 * kt + 16 * st, 32 * dt, lane);
-            oacc[dt] = mma32(af, bf, oacc[dt]);
-            if (PREC == 1) oacc[dt] = mma32(af, bl, oacc[dt]);
-          }
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8 af = ld_tr32(cV, LD, 32 * kt + 16 * st, 32 * dt, lane);
+          oacc[dt] = mma32(af, bf, oacc[dt]);
+          if (PREC == 1) oacc[dt] = mma32(af, bl, oacc[dt]);
         }
       }
   };

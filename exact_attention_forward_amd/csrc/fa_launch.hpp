@@ -13,12 +13,25 @@ namespace fa {
 template <typename TIn, int HD>
 struct TileCfg;
 
-// bfloat16 kernels use 32x32 tiles: NW waves of 32 rows each.
+// bfloat16 kernels use 32x32 tiles: NW waves of 32 rows each.  The block
+// sizes can be overridden at compile time for tuning sweeps.
+#ifndef FA_FWD_BC64
+#define FA_FWD_BC64 64
+#endif
+#ifndef FA_DQ_BC64
+#define FA_DQ_BC64 64
+#endif
+#ifndef FA_DKV_BQ64
+#define FA_DKV_BQ64 64
+#endif
+#ifndef FA_NW64
+#define FA_NW64 4
+#endif
 template <int HD>
 struct TileCfg32 {
-  static constexpr int FWD_NW = 4, FWD_BC = HD <= 64 ? 128 : 64;
-  static constexpr int DQ_NW = 4, DQ_BC = 64;
-  static constexpr int DKV_NW = 4, DKV_BQ = 64;
+  static constexpr int FWD_NW = HD <= 64 ? FA_NW64 : 4, FWD_BC = HD <= 64 ? FA_FWD_BC64 : 64;
+  static constexpr int DQ_NW = HD <= 64 ? FA_NW64 : 4, DQ_BC = HD <= 64 ? FA_DQ_BC64 : 64;
+  static constexpr int DKV_NW = HD <= 64 ? FA_NW64 : 4, DKV_BQ = HD <= 64 ? FA_DKV_BQ64 : 64;
 };
 
 template <int HD>
