@@ -43,7 +43,10 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs
   const int n = lane & 31, h = lane >> 5;
 
   const int nqt = (T + BR - 1) / BR;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int total = nqt * a.B * H;
+  for (int round = 0;; ++round) {
+    const int w = persistent_item(round, total);
+    if (w < 0) break;
   const int bh = w / nqt;
   const int qt = nqt - 1 - (w % nqt);
   const int b = bh / H, hh = bh % H;
@@ -160,6 +163,7 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs
         *reinterpret_cast<f32x4*>(out + 32 * dt + 8 * bb + 4 * h) = v4;
       }
   }
+  }
 }
 
 template <int HD, bool CAUSAL, int PREC, int NW, int BQ>
@@ -184,7 +188,10 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
   const int n = lane & 31, h = lane >> 5;
 
   const int nkt = (T + BK - 1) / BK;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int total = nkt * a.B * H;
+  for (int round = 0;; ++round) {
+    const int w = persistent_item(round, total);
+    if (w < 0) break;
   const int bh = w / nkt;
   const int kt = w % nkt;
   const int b = bh / H, hh = bh % H;
@@ -239,26 +246,32 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
   load_ld(qb0, 0);
   __syncthreads();
 
+  // One query block as a three-stage software pipeline over its 32-row
+  // tiles: A(t) = the S and dP products, B(t) = P and dS in registers (VALU and
+  // exp), C(t) = the dV and dK products.  The order A(t+1), B(t), C(t) keeps
+  // independent matrix and vector work next to each other in one basic block.
   auto block = [&](const bf16_t* cQ, const bf16_t* cG, const float* cL, const float* cD, const int q0,
                    auto masked) {
     constexpr bool MASK = decltype(masked)::value;
-    // a 32-row tile is dead when every query in it precedes every key of the wave
-    auto live = [&](int it) { return !(MASK && CAUSAL) || (q0 + 32 * it + 31 >= c0); };
-    f32x16 s[NIT], dp[NIT];
+    f32x16 s[2], dp[2];
+    auto stage_a = [&](int it, f32x16& sa, f32x16& da) {
+      sa = zero16();
+      da = zero16();
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) s[it] = dp[it] = zero16();
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int it = 0; it < NIT; ++it)
-        if (live(it)) {
-          s[it] = mma32(ld_row32(cQ, LD, 32 * it, 16 * ks, n, h), kf[ks], s[it]);
-          dp[it] = mma32(ld_row32(cG, LD, 32 * it, 16 * ks, n, h), vf[ks], dp[it]);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        sa = mma32(ld_row32(cQ, LD, 32 * it, 16 * ks, n, h), kf[ks], sa);
+        da = mma32(ld_row32(cG, LD, 32 * it, 16 * ks, n, h), vf[ks], da);
+      }
+    };
+    stage_a(0, s[0], dp[0]);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      if (!live(it)) continue;
+      f32x16& sc = s[it & 1];
+      f32x16& dc = dp[it & 1];
+      if (it + 1 < NIT) stage_a(it + 1, s[(it + 1) & 1], dp[(it + 1) & 1]);
+      // stage B: P = exp2(S c - L), dS = P (dP - D), packed for the products
       const int lim = lo - (q0 + 32 * it);
+      bf16x8 bp[2], bs[2], bpl[2], bsl[2];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const int rr = 32 * it + 8 * bb + 4 * h;
@@ -267,38 +280,36 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = 4 * bb + r;
-          float p = fast_exp2(fmaf(s[it][e], c2, -lv[r]));
+          float p = fast_exp2(fmaf(sc[e], c2, -lv[r]));
           if (MASK && CAUSAL && 8 * bb + r < lim) p = 0.f;
-          s[it][e] = p;
-          dp[it][e] = p * (dp[it][e] - d4[r]);
+          sc[e] = p;
+          dc[e] = p * (dc[e] - d4[r]);
         }
       }
-    }
 #pragma unroll
-    for (int it = 0; it < NIT; ++it)
-      if (live(it)) {
+      for (int st = 0; st < 2; ++st) {
+        bp[st] = pack32(sc, st);
+        bs[st] = pack32(dc, st);
+        if (PREC == 1) {
+          bpl[st] = pack32_lo(sc, st);
+          bsl[st] = pack32_lo(dc, st);
+        }
+      }
+      // stage C
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16x8 bp = pack32(s[it], st);
-          const bf16x8 bs = pack32(dp[it], st);
-          bf16x8 bpl, bsl;
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8 ga = ld_tr32(cG, LD, 32 * it + 16 * st, 32 * dt, lane);
+          const bf16x8 qa = ld_tr32(cQ, LD, 32 * it + 16 * st, 32 * dt, lane);
+          dv[dt] = mma32(ga, bp[st], dv[dt]);
+          dk[dt] = mma32(qa, bs[st], dk[dt]);
           if (PREC == 1) {
-            bpl = pack32_lo(s[it], st);
-            bsl = pack32_lo(dp[it], st);
-          }
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8 ga = ld_tr32(cG, LD, 32 * it + 16 * st, 32 * dt, lane);
-            const bf16x8 qa = ld_tr32(cQ, LD, 32 * it + 16 * st, 32 * dt, lane);
-            dv[dt] = mma32(ga, bp, dv[dt]);
-            dk[dt] = mma32(qa, bs, dk[dt]);
-            if (PREC == 1) {
-              dv[dt] = mma32(ga, bpl, dv[dt]);
-              dk[dt] = mma32(qa, bsl, dk[dt]);
-            }
+            dv[dt] = mma32(ga, bpl[st], dv[dt]);
+            dk[dt] = mma32(qa, bsl[st], dk[dt]);
           }
         }
-      }
+    }
   };
 
   for (int qb = qb0; qb < nqb; ++qb) {
@@ -336,6 +347,7 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
         *reinterpret_cast<f32x4*>(outk + 32 * dt + 8 * bb + 4 * h) = k4;
         *reinterpret_cast<f32x4*>(outv + 32 * dt + 8 * bb + 4 * h) = v4;
       }
+  }
   }
 }
 

@@ -59,6 +59,22 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return x * q + (x < rem ? x : rem) + slot;
 }
 
+// Persistent-workgroup schedule.  Logical work items [0, total) are split into
+// 8 contiguous ranges, one per XCD (workgroup w runs on XCD w % 8).  Round r
+// hands the XCD's workgroups consecutive items of its range, in reverse
+// order on odd rounds, so long and short causal items pair up.  Returns the
+// item for (round r, this workgroup), or -1 once the range is exhausted; the
+// result is uniform across the workgroup.
+__device__ __forceinline__ int persistent_item(int r, int total) {
+  const int G = gridDim.x, w = blockIdx.x;
+  const int x = w % 8, slot = w / 8;
+  const int nslots = (G - x + 7) / 8;
+  const int q = total / 8, rem = total % 8;
+  const int start = x * q + (x < rem ? x : rem), count = q + (x < rem ? 1 : 0);
+  const int local = r * nslots + ((r & 1) ? nslots - 1 - slot : slot);
+  return local < count ? start + local : -1;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA policies.  Each supplies:
 //   KS     contraction length of one instruction

@@ -23,6 +23,7 @@ namespace fa {
 
 template <int HD, bool CAUSAL, int PREC, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void fwd32_kernel(FwdArgs a) {
+  // Persistent: the grid is sized to the resident workgroups and each loops over work items.
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
   constexpr int LD = HD + 8;
@@ -41,7 +42,10 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void fwd32_kernel(FwdArg
   const int n = lane & 31, h = lane >> 5;
 
   const int nqt = (T + BR - 1) / BR;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int total = nqt * a.B * H;
+  for (int round = 0;; ++round) {
+    const int w = persistent_item(round, total);
+    if (w < 0) break;
   const int bh = w / nqt;
   const int qt = nqt - 1 - (w % nqt);
   const int b = bh / H, hh = bh % H;
@@ -177,6 +181,7 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void fwd32_kernel(FwdArg
         *reinterpret_cast<f32x4*>(O + 32 * dt + 8 * bb + 4 * h) = v4;
       }
     if (h == 0) a.lse[(size_t)bh * T + row] = l > 0.f ? (mrow + log2f(l)) * kLn2 : -INFINITY;
+  }
   }
 }
 

@@ -55,13 +55,39 @@ struct TileCfg<bf16_t, 128> {
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? 0 : -5; }
 
+// Compute units of the current device (cached per device id).
+inline int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Grid for a persistent kernel: every resident workgroup slot, at most one per item.
+template <typename K>
+inline long persistent_grid(K kernel, int threads, long items) {
+  static int per_cu = 0;  // one value per kernel instantiation
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
+    per_cu = n;
+  }
+  const long slots = (long)per_cu * device_cus();
+  return items < slots ? items : slots;
+}
+
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_fwd(const FwdArgs& a, hipStream_t s) {
   if constexpr (sizeof(TIn) == 2) {
     using C = TileCfg32<HD>;
-    const long grid = (long)((a.T + C::FWD_NW * 32 - 1) / (C::FWD_NW * 32)) * a.B * a.H;
-    hipLaunchKernelGGL((fwd32_kernel<HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC>), dim3((unsigned)grid),
-                       dim3(C::FWD_NW * 64), 0, s, a);
+    auto* k = &fwd32_kernel<HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC>;
+    const long items = (long)((a.T + C::FWD_NW * 32 - 1) / (C::FWD_NW * 32)) * a.B * a.H;
+    hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::FWD_NW * 64, items)), dim3(C::FWD_NW * 64), 0, s, a);
     return launch_status();
   }
   using C = TileCfg<TIn, HD>;
@@ -85,9 +111,9 @@ template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_dq(const BwdArgs& a, hipStream_t s) {
   if constexpr (sizeof(TIn) == 2) {
     using C = TileCfg32<HD>;
-    const long grid = (long)((a.T + C::DQ_NW * 32 - 1) / (C::DQ_NW * 32)) * a.B * a.H;
-    hipLaunchKernelGGL((dq32_kernel<HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC>), dim3((unsigned)grid),
-                       dim3(C::DQ_NW * 64), 0, s, a);
+    auto* k = &dq32_kernel<HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC>;
+    const long items = (long)((a.T + C::DQ_NW * 32 - 1) / (C::DQ_NW * 32)) * a.B * a.H;
+    hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DQ_NW * 64, items)), dim3(C::DQ_NW * 64), 0, s, a);
     return launch_status();
   }
   using C = TileCfg<TIn, HD>;
@@ -102,9 +128,9 @@ template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_dkv(const BwdArgs& a, hipStream_t s) {
   if constexpr (sizeof(TIn) == 2) {
     using C = TileCfg32<HD>;
-    const long grid = (long)((a.T + C::DKV_NW * 32 - 1) / (C::DKV_NW * 32)) * a.B * a.H;
-    hipLaunchKernelGGL((dkv32_kernel<HD, CAUSAL, PREC, C::DKV_NW, C::DKV_BQ>), dim3((unsigned)grid),
-                       dim3(C::DKV_NW * 64), 0, s, a);
+    auto* k = &dkv32_kernel<HD, CAUSAL, PREC, C::DKV_NW, C::DKV_BQ>;
+    const long items = (long)((a.T + C::DKV_NW * 32 - 1) / (C::DKV_NW * 32)) * a.B * a.H;
+    hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DKV_NW * 64, items)), dim3(C::DKV_NW * 64), 0, s, a);
     return launch_status();
   }
   using C = TileCfg<TIn, HD>;
