@@ -4,16 +4,17 @@ Workload: GPT-2-medium-shaped causal attention, B=64 H=16 T=1024 hd=64,
 bfloat16 inputs drawn N(0, 1) (seeded, synthetic), float32 accumulation and
 outputs, P and dS rounded to bfloat16 for their matrix products.
 
-One step = fa_forward, then the three backward stages (fa_backward_delta,
-fa_backward_dq, fa_backward_dkv -- exactly what fa_backward runs), with every
-input already resident in HBM.  W untimed warm-up steps, then K timed steps
+One step = fa_forward, then the two backward stages (fa_backward_dq_delta,
+fa_backward_dkv -- exactly what fa_backward runs), with every input already
+resident in HBM.  W untimed warm-up steps, then K timed steps
 between two device synchronisations; HIP events on the launch stream time each
 kernel inside the timed region.
 
 The metric counts 14*hd flops per (query, visible key) pair, B*H*T^2/2 pairs
 for the causal mask.  The roofline object describes the kernel with the
 largest share of the step; its algorithmic flops are the products it must
-execute (forward 4*hd, dQ kernel 6*hd, dK/dV kernel 8*hd per pair).
+execute (forward 4*hd, dQ kernel 6*hd, dK/dV kernel 8*hd per pair; the dQ
+kernel's 2*hd flops per row for D are not counted).
 
 The CPU baseline times the float64 oracle on the host cores over a bounded
 sample of the same workload (whole heads), and compares those heads of the
@@ -39,8 +40,8 @@ sys.path.insert(0, str(ROOT))
 METRIC = "attention fwd+bwd TFLOP/s (% MFMA peak), causal B64 H16 T1024 hd64, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-STAGES = ("fwd", "delta", "dq", "dkv")
-KERNEL_NAMES = {"fwd": "fwd_kernel", "delta": "delta_kernel", "dq": "dq_kernel", "dkv": "dkv_kernel"}
+STAGES = ("fwd", "dq", "dkv")
+KERNEL_NAMES = {"fwd": "fwd32_kernel", "dq": "dq32_kernel", "dkv": "dkv32_kernel"}
 COPY_BYTES = 1 << 30
 
 
@@ -109,15 +110,12 @@ def main() -> int:
         fa.check(fa.fa_forward(q, k, v, o, lse, B, H, T, hd, sc, 1, dt, prec, stream))
         if ev is not None:
             ev[1].record(stream)
-        fa.check(fa.fa_backward_delta(o, do, delta, B, H, T, hd, dt, stream))
+        fa.check(fa.fa_backward_dq_delta(q, k, v, o, lse, do, dq, delta, B, H, T, hd, sc, 1, dt, prec, stream))
         if ev is not None:
             ev[2].record(stream)
-        fa.check(fa.fa_backward_dq(q, k, v, lse, do, delta, dq, B, H, T, hd, sc, 1, dt, prec, stream))
-        if ev is not None:
-            ev[3].record(stream)
         fa.check(fa.fa_backward_dkv(q, k, v, lse, do, delta, dk, dv, B, H, T, hd, sc, 1, dt, prec, stream))
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
 
     if args.counters:
         x = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
@@ -135,7 +133,7 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -147,7 +145,7 @@ def main() -> int:
     per = {s: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, s in enumerate(STAGES)}
     pairs = B * H * T * T / 2
     counted = 14 * hd * pairs
-    algo_flops = {"fwd": 4 * hd * pairs, "delta": 0.0, "dq": 6 * hd * pairs, "dkv": 8 * hd * pairs}
+    algo_flops = {"fwd": 4 * hd * pairs, "dq": 6 * hd * pairs, "dkv": 8 * hd * pairs}
     value = counted / (ms_step * 1e-3) / 1e12
 
     dom = max(("fwd", "dq", "dkv"), key=lambda s: per[s])

@@ -34,6 +34,7 @@ SIGNATURES = {
     "fa_backward_delta": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_backward_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_backward_dkv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_backward_dq_delta": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_is_supported": (_I, [_I, _I]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -111,6 +112,11 @@ def fa_backward_dq(q, k, v, lse, dO, delta, dq, B, H, T, hd, scale, causal, dtyp
 def fa_backward_dkv(q, k, v, lse, dO, delta, dk, dv, B, H, T, hd, scale, causal, dtype, prec, stream) -> int:
     return lib().fa_backward_dkv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dO), _ptr(delta), _ptr(dk), _ptr(dv), B,
                                  H, T, hd, scale, int(causal), dtype, prec, _stream(stream))
+
+
+def fa_backward_dq_delta(q, k, v, o, lse, dO, dq, delta, B, H, T, hd, scale, causal, dtype, prec, stream) -> int:
+    return lib().fa_backward_dq_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(delta), B,
+                                      H, T, hd, scale, int(causal), dtype, prec, _stream(stream))
 
 
 def fa_is_supported(hd, dtype) -> int:

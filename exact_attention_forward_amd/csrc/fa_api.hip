@@ -179,6 +179,22 @@ int fa_backward_dkv(const void* q, const void* k, const void* v, const float* ls
   return run(fa::kDkv, hd, dtype, prec, causal != 0, &a, stream);
 }
 
+int fa_backward_dq_delta(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                         const void* dO, float* dq, float* delta, int B, int H, int T, int hd, float scale,
+                         int causal, fa_dtype dtype, fa_precision prec, void* stream) {
+  int st = check_common(B, H, T, hd, dtype, prec);
+  if (st) return st;
+  if ((st = check_scale(scale, causal))) return st;
+  const void* ptrs[] = {q, k, v, o, lse, dO, dq, delta};
+  if ((st = check_ptrs(ptrs, 8))) return st;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_BF16 ? 2 : 4, nr = (size_t)B * H * T * 4;
+  const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}, {o, n * 4}, {lse, nr}, {dO, n * es}};
+  const Buf out[] = {{dq, n * 4}, {delta, nr}};
+  if ((st = check_alias(in, 6, out, 2))) return st;
+  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dO, dq, nullptr, nullptr, delta, B, H, T, scale);
+  return run(fa::kDqDelta, hd, dtype, prec, causal != 0, &a, stream);
+}
+
 int fa_backward(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dO,
                 float* dq, float* dk, float* dv, float* delta, int B, int H, int T, int hd, float scale, int causal,
                 fa_dtype dtype, fa_precision prec, void* stream) {
@@ -191,8 +207,8 @@ int fa_backward(const void* q, const void* k, const void* v, const float* o, con
   const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}, {o, n * 4}, {lse, nr}, {dO, n * es}};
   const Buf out[] = {{dq, n * 4}, {dk, n * 4}, {dv, n * 4}, {delta, nr}};
   if ((st = check_alias(in, 6, out, 4))) return st;
-  if ((st = fa_backward_delta(o, dO, delta, B, H, T, hd, dtype, stream))) return st;
-  if ((st = fa_backward_dq(q, k, v, lse, dO, delta, dq, B, H, T, hd, scale, causal, dtype, prec, stream))) return st;
+  if ((st = fa_backward_dq_delta(q, k, v, o, lse, dO, dq, delta, B, H, T, hd, scale, causal, dtype, prec, stream)))
+    return st;
   return fa_backward_dkv(q, k, v, lse, dO, delta, dk, dv, B, H, T, hd, scale, causal, dtype, prec, stream);
 }
 

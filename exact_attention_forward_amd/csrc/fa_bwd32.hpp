@@ -23,7 +23,10 @@
 
 namespace fa {
 
-template <int HD, bool CAUSAL, int PREC, int NW, int BC>
+// FUSE_D: compute D_i = <dO_i, O_i> for the tile's rows from O (float32) and
+// the dO fragments already in registers, and write it to a.delta, instead of
+// reading a.delta (the pre-pass folded into this kernel).
+template <int HD, bool CAUSAL, int PREC, int NW, int BC, bool FUSE_D>
 __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
@@ -69,10 +72,26 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs
     gf[ks] = ld_row_global32(dO, rs, row, T, 16 * ks, h);
   }
   float l2 = INFINITY, dd = 0.f;
+  if (FUSE_D) {
+    // lane (n, h) holds dO[row][16 ks + 8h .. +7]; its partner (n, 1-h) the rest
+    float part = 0.f;
+    if (row < T) {
+      const float* orow = a.o + base + (size_t)row * rs;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + 16 * ks + 8 * h);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + 16 * ks + 8 * h + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part += o0[e] * (float)gf[ks][e] + o1[e] * (float)gf[ks][4 + e];
+      }
+    }
+    dd = part + __shfl_xor(part, 32);
+    if (row < T && h == 0) a.delta[(size_t)bh * T + row] = dd;
+  }
   if (row < T) {
     l2 = a.lse[(size_t)bh * T + row] * kLog2e;
     if (l2 == -INFINITY) l2 = INFINITY;  // a row that saw no key has zero gradient
-    dd = a.delta[(size_t)bh * T + row];
+    if (!FUSE_D) dd = a.delta[(size_t)bh * T + row];
   }
   f32x16 acc[NDT];
 #pragma unroll

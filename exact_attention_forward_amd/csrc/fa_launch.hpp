@@ -107,14 +107,18 @@ int run_delta(const BwdArgs& a, hipStream_t s) {
   return launch_status();
 }
 
-template <typename TIn, int HD, bool CAUSAL, int PREC>
+template <typename TIn, int HD, bool CAUSAL, int PREC, bool FUSE_D = false>
 int run_dq(const BwdArgs& a, hipStream_t s) {
   if constexpr (sizeof(TIn) == 2) {
     using C = TileCfg32<HD>;
-    auto* k = &dq32_kernel<HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC>;
+    auto* k = &dq32_kernel<HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC, FUSE_D>;
     const long items = (long)((a.T + C::DQ_NW * 32 - 1) / (C::DQ_NW * 32)) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DQ_NW * 64, items)), dim3(C::DQ_NW * 64), 0, s, a);
     return launch_status();
+  }
+  if constexpr (FUSE_D) {  // float32 path: the pre-pass, then the dQ kernel
+    const int st = run_delta<TIn, HD>(a, s);
+    if (st) return st;
   }
   using C = TileCfg<TIn, HD>;
   constexpr int BR = C::DQ_NW * 16 * C::DQ_MR;
@@ -141,13 +145,14 @@ int run_dkv(const BwdArgs& a, hipStream_t s) {
   return launch_status();
 }
 
-enum Stage { kFwd = 0, kDq = 1, kDkv = 2 };
+enum Stage { kFwd = 0, kDq = 1, kDkv = 2, kDqDelta = 3 };
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_stage(int stage, const void* args, hipStream_t s) {
   switch (stage) {
     case kFwd: return run_fwd<TIn, HD, CAUSAL, PREC>(*static_cast<const FwdArgs*>(args), s);
     case kDq: return run_dq<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);
+    case kDqDelta: return run_dq<TIn, HD, CAUSAL, PREC, true>(*static_cast<const BwdArgs*>(args), s);
     default: return run_dkv<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);
   }
 }

@@ -77,8 +77,8 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
 /*
  * Backward pass with recomputation (backward notes, "The math (FA2 backward
  * with recompute)"): from the forward's o and lse and the upstream gradient
- * dO = d loss / d o, writes dq, dk, dv.  Runs the three stages below in order
- * on `stream`.
+ * dO = d loss / d o, writes dq, dk, dv.  Runs fa_backward_dq_delta, then
+ * fa_backward_dkv, in order on `stream`.
  *   q, k, v, dO  [B, T, H, hd] inputs of `dtype`
  *   o            [B, T, H, hd] float32, the forward output for these inputs
  *   lse          [B, H, T] float32, the forward log-sum-exp
@@ -91,8 +91,9 @@ int fa_backward(const void* q, const void* k, const void* v, const float* o, con
                 fa_dtype dtype, fa_precision prec, void* stream);
 
 /*
- * The three backward stages, for callers that schedule them separately.
- * fa_backward == fa_backward_delta; fa_backward_dq; fa_backward_dkv.
+ * The backward stages, for callers that schedule them separately.
+ * fa_backward == fa_backward_dq_delta; fa_backward_dkv, and
+ * fa_backward_dq_delta == fa_backward_delta; fa_backward_dq.
  *
  * fa_backward_delta: delta[b, h, i] = <dO[b, i, h, :], o[b, i, h, :]>, the
  * pre-pass of the backward notes ("Why the WGSL kernel isn't shipped this
@@ -108,6 +109,16 @@ int fa_backward_delta(const float* o, const void* dO, float* delta, int B, int H
 int fa_backward_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO,
                    const float* delta, float* dq, int B, int H, int T, int hd, float scale, int causal,
                    fa_dtype dtype, fa_precision prec, void* stream);
+
+/*
+ * fa_backward_dq_delta: fa_backward_delta and fa_backward_dq in one pass: each
+ * query tile computes D for its rows from o and dO (the pre-pass of the
+ * backward notes), writes it to delta, and produces dq (the dQ kernel of
+ * option 3).  Outputs: dq and delta.
+ */
+int fa_backward_dq_delta(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                         const void* dO, float* dq, float* delta, int B, int H, int T, int hd, float scale,
+                         int causal, fa_dtype dtype, fa_precision prec, void* stream);
 
 /*
  * fa_backward_dkv: one workgroup per key tile, walking every query that can

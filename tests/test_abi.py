@@ -115,6 +115,12 @@ def test_backward_validation(lib, kw, status):
 
 
 def test_stage_entry_points_validate(lib):
+    assert fa.fa_backward_dq_delta(P[0], P[1], P[2], P[3], P[4], P[5], P[6], None, 1, 2, 8, 64, 0.1, 1, fa.FA_F32, 0,
+                                   None) == fa.FA_ERR_ARG
+    assert fa.fa_backward_dq_delta(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[3], 1, 2, 8, 64, 0.1, 1, fa.FA_F32, 0,
+                                   None) == fa.FA_ERR_ALIAS
+    assert fa.fa_backward_dq_delta(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 1, 2, 8, 48, 0.1, 1, fa.FA_F32, 0,
+                                   None) == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_backward_delta(P[3], P[5], None, 1, 2, 8, 64, fa.FA_F32, None) == fa.FA_ERR_ARG
     assert fa.fa_backward_delta(P[3], P[5], P[3], 1, 2, 8, 64, fa.FA_F32, None) == fa.FA_ERR_ALIAS
     assert fa.fa_backward_dq(P[0], P[1], P[2], P[4], P[5], P[9], P[6], 1, 2, 8, 24, 0.1, 1, fa.FA_F32, 0,

@@ -152,8 +152,20 @@ def test_stages_equal_combined_backward():
         fa.check(fa.fa_backward_dq(q, k, v, ref["L"], do, delta, dq, B, H, T, hd, c.scale, 1, fa.FA_BF16, 0, s))
         fa.check(fa.fa_backward_dkv(q, k, v, ref["L"], do, delta, dk, dv, B, H, T, hd, c.scale, 1, fa.FA_BF16, 0, s))
     torch.cuda.synchronize()
-    assert torch.equal(delta, ref["D"]) and torch.equal(dq, ref["dQ"])
-    assert torch.equal(dk, ref["dK"]) and torch.equal(dv, ref["dV"])
+    # fa_backward fuses the pre-pass into the dQ kernel and sums D in another
+    # order; a change of D in the last bits can flip the bfloat16 rounding of
+    # single dS values, so the separate path is held to the oracle bar instead
+    assert float((delta - ref["D"]).abs().max()) <= 1e-5
+    sep = dict(ref)
+    sep.update(dQ=dq, dK=dk, dV=dv, D=delta)
+    err = full_errors(c, sep)
+    assert_within(err, BF16_TOL, "separate stages")
+    # the fused stage reproduces fa_backward exactly
+    dq2, delta2 = torch.full_like(dq, float("nan")), torch.full_like(delta, float("nan"))
+    fa.check(fa.fa_backward_dq_delta(q, k, v, ref["O"], ref["L"], do, dq2, delta2, B, H, T, hd, c.scale, 1, fa.FA_BF16,
+                                     0, None))
+    torch.cuda.synchronize()
+    assert torch.equal(dq2, ref["dQ"]) and torch.equal(delta2, ref["D"])
 
 
 def test_invalid_call_writes_nothing():
