@@ -33,7 +33,8 @@ struct FwdArgs {
   float* o;
   float* lse;
   int B, H, T;
-  float c2;  // scale * log2(e)
+  float c2;                    // scale * log2(e)
+  unsigned one2 = 0x3F803F80u;  // bfloat16 pair (1, 1): a scalar operand for row sums by dot products
 };
 
 // PREC: 0 = operands rounded to bfloat16 (or exact f32), 1 = P split into a

@@ -2,17 +2,26 @@
 //
 // Same algorithm as fwd_kernel ("Flash Attention 2 -- forward pass notes",
 // section "Loop (per (b, h, Q-tile))"): online softmax over streamed K/V
-// blocks, causal block skip, O and L = m + ln l written once.  Each wave owns
-// 32 query rows; lane (n, h) owns row n of the wave together with lane
-// (n, 1-h), so the row max and row sum need one exchange across lane halves.
+// blocks, causal block skip, O and L = m + ln l written once.
+//  * Each wave owns MS sub-tiles of 32 query rows.  Lane (n, h) owns row n of
+//    every sub-tile together with lane (n, 1-h), so the row max and row sum
+//    need one exchange across lane halves (v_permlane32_swap).
 //  * S^T = K Q^T per 32-key tile: K from the LDS block, Q^T from registers.
-//  * O^T += V^T P^T: P^T straight from the S^T registers (see fa_mfma32.hpp),
-//    V^T by LDS transpose reads of the row-major V block.
-//  * Every block runs straight-line code, so the independent MFMA chains of
-//    the block interleave; blocks crossing the causal diagonal or the end of
-//    the sequence add an element-wise mask before the row max.
-//  * The rescale of O by alpha is skipped when no row of the wave raised its
-//    running max in the block.
+//    O^T += V^T P^T: P^T straight from the S^T registers (see fa_mfma32.hpp),
+//    V^T by LDS transpose reads of the row-major V block.  Every K or V
+//    operand read from LDS feeds the products of all MS sub-tiles, and the
+//    vector-ALU softmax of one sub-tile overlaps the matrix products of the
+//    other.
+//  * The running max is a reference value for the exponentials, not
+//    necessarily the exact row max: it is raised (and O, l rescaled) only when
+//    a block's max exceeds it by more than 2^8 in the exponential's units.
+//    The normalised result is the same for any reference (O = sum p v / sum p
+//    with the same p in both), and weights up to 2^8 stay far from overflow.
+//  * Row sums add the bfloat16 weights that enter the P V product (dot
+//    products with (1, 1)), so O is normalised by exactly the weights used.
+//  * Blocks crossing the causal diagonal or the end of the sequence apply an
+//    element-wise -inf mask to the raw scores before the row max; sub-tiles
+//    wholly above the diagonal skip the block.
 #pragma once
 #include <type_traits>
 
@@ -21,17 +30,67 @@
 
 namespace fa {
 
-template <int HD, bool CAUSAL, int PREC, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void fwd32_kernel(FwdArgs a) {
+// Max over lanes l and l ^ 32 (the two halves of one row).
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Adds the eight bfloat16 values of an operand fragment to two partial sums.
+// The pairs are taken with shufflevector: reinterpreting the fragment as four
+// 32-bit words before the dot products was mis-lowered by the compiler (the
+// same register fed every product).
+__device__ __forceinline__ void sum8(bf16x8 v, unsigned one2, float& acc0, float& acc1) {
+  const bf16x2 o = __builtin_bit_cast(bf16x2, one2);
+  acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), o, acc0, false);
+  acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), o, acc1, false);
+  acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), o, acc0, false);
+  acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), o, acc1, false);
+}
+
+// Exponent headroom (base 2) before the reference max is raised.
+constexpr float kRescaleSlack = 8.f;
+
+// Max of the 16 elements of a C tile, as a shallow tree.
+__device__ __forceinline__ float tile_max(const f32x16& x) {
+  float m[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) m[g] = fmaxf(fmaxf(x[4 * g], x[4 * g + 1]), fmaxf(x[4 * g + 2], x[4 * g + 3]));
+  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+}
+
+// Sub-tile u of wave w covers rows 32 w (u = 0) and 32 (2 NW - 1 - w) (u = 1)
+// of the workgroup's tile, so under the causal mask every wave has the same
+// number of (row, key) pairs to visit.
+template <int NW, int MS>
+__device__ __forceinline__ int subtile_row(int wave, int u) {
+  return MS == 1 ? 32 * wave : (u == 0 ? 32 * wave : 32 * (2 * NW - 1 - wave));
+}
+
+#ifndef FA_FWD_WPE64
+#define FA_FWD_WPE64 2
+#endif
+template <int HD, bool CAUSAL, int PREC, int NW, int BC, int MS>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(HD <= 64 ? FA_FWD_WPE64 : 1, HD <= 64 ? FA_FWD_WPE64 : 1)))
+void fwd32_kernel(FwdArgs a) {
   // Persistent: the grid is sized to the resident workgroups and each loops over work items.
   constexpr int NT = NW * 64;
-  constexpr int BR = NW * 32;
+  constexpr int BR = NW * 32 * MS;
   constexpr int LD = HD + 8;
   constexpr int NDT = HD / 32;  // 32-wide output tiles
   constexpr int NKS = HD / 16;  // product steps over the head dim
   constexpr int NKT = BC / 32;  // 32-key tiles per block
   static_assert(HD % 32 == 0 && BC % 32 == 0, "tile shape");
   static_assert(2 * 2 * BC * LD * 2 <= 160 * 1024, "LDS budget");
+  static_assert(MS == 1 || MS == 2, "one or two sub-tiles per wave");
+  using Copy = TileStream<HD, BC, NT>;
 
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][BC * LD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][BC * LD];
@@ -40,148 +99,215 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void fwd32_kernel(FwdArg
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
+  const unsigned one2 = a.one2;
+  const float c2 = a.c2;
+  const size_t rs = (size_t)H * HD;
+  unsigned goff[Copy::PER];  // byte offsets of this thread's copy vectors within a block
+#pragma unroll
+  for (int p = 0; p < Copy::PER; ++p) goff[p] = (unsigned)((Copy::vrow(tid, p) * rs + Copy::vcol(tid, p)) * 2);
 
   const int nqt = (T + BR - 1) / BR;
   const int total = nqt * a.B * H;
   for (int round = 0;; ++round) {
     const int w = persistent_item(round, total);
     if (w < 0) break;
-  const int bh = w / nqt;
-  const int qt = nqt - 1 - (w % nqt);
-  const int b = bh / H, hh = bh % H;
-  const size_t rs = (size_t)H * HD;
-  const size_t base = ((size_t)b * T * H + hh) * HD;
-  const bf16_t* Q = static_cast<const bf16_t*>(a.q) + base;
-  const bf16_t* K = static_cast<const bf16_t*>(a.k) + base;
-  const bf16_t* V = static_cast<const bf16_t*>(a.v) + base;
-  const int i0 = qt * BR;
-  const int r0 = i0 + wave * 32;
-  const int row = r0 + n;
-  const float c2 = a.c2;
-  // Largest visible key of this lane's row, minus the lane-half offset of the
-  // C layout: element e of a tile starting at key jt is masked iff
-  // 8*(e/4) + e%4 > vis - jt.
-  const int vis = (CAUSAL ? min(row, T - 1) : T - 1) - 4 * h;
+    const int bh = w / nqt;
+    const int qt = nqt - 1 - (w % nqt);
+    const int b = bh / H, hh = bh % H;
+    const size_t base = ((size_t)b * T * H + hh) * HD;
+    const bf16_t* Q = static_cast<const bf16_t*>(a.q) + base;
+    const bf16_t* K = static_cast<const bf16_t*>(a.k) + base;
+    const bf16_t* V = static_cast<const bf16_t*>(a.v) + base;
+    const int i0 = qt * BR;
+    const int nkb = CAUSAL ? ((min(i0 + BR, T) - 1) / BC + 1) : (T + BC - 1) / BC;
 
-  bf16x8 qf[NKS];
+    bf16x8 qf[MS][NKS];
+    f32x16 oacc[MS][NDT];
+    float mref[MS], ls0[MS], ls1[MS];
+    int r0[MS], vis[MS], lastb[MS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qf[ks] = ld_row_global32(Q, rs, row, T, 16 * ks, h);
-
-  f32x16 oacc[NDT];
+    for (int u = 0; u < MS; ++u) {
+      r0[u] = i0 + subtile_row<NW, MS>(wave, u);
+      const int row = r0[u] + n;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = zero16();
-  float mrow = -INFINITY, lrow = 0.f;
-
-  const int last_row = min(i0 + BR, T) - 1;
-  const int nkb = CAUSAL ? (last_row / BC + 1) : (T + BC - 1) / BC;
-
-  TileCopy<bf16_t, HD, BC, NT> ck, cv;
-  ck.load(K, rs, 0, T, tid);
-  cv.load(V, rs, 0, T, tid);
-  ck.store(sK[0], LD, tid);
-  cv.store(sV[0], LD, tid);
-  __syncthreads();
-
-  auto block = [&](const bf16_t* cK, const bf16_t* cV, const int j0, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    f32x16 s[NKT];
+      for (int ks = 0; ks < NKS; ++ks) qf[u][ks] = ld_row_global32(Q, rs, row, T, 16 * ks, h);
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) s[kt] = zero16();
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) s[kt] = mma32(ld_row32(cK, LD, 32 * kt, 16 * ks, n, h), qf[ks], s[kt]);
-    if (MASK) {
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        const int lim = vis - (j0 + 32 * kt);
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (8 * (e >> 2) + (e & 3) > lim) s[kt][e] = -INFINITY;
-      }
+      for (int dt = 0; dt < NDT; ++dt) oacc[u][dt] = zero16();
+      mref[u] = -INFINITY;
+      ls0[u] = ls1[u] = 0.f;
+      // Largest visible key of this lane's row, minus the lane-half offset of
+      // the C layout: element e of a tile starting at key jt is masked iff
+      // 8*(e/4) + e%4 > vis - jt.
+      vis[u] = (CAUSAL ? min(row, T - 1) : T - 1) - 4 * h;
+      lastb[u] = r0[u] >= T ? -1 : (CAUSAL ? min(r0[u] + 31, T - 1) / BC : nkb - 1);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrow, mx * c2);
-    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-    const bool grew = mnew > mrow;
-    const float alpha = (mrow == -INFINITY) ? 0.f : fast_exp2(mrow - mnew);
-    mrow = mnew;
-    // P = exp2(s c2 - m); the row sum adds the unrounded float weights.
-    bf16x8 pk[NKT][2];
-    float ls = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[kt][e] = fast_exp2(fmaf(s[kt][e], c2, -muse));
-        ls += s[kt][e];
+
+    Copy ck, cv;
+    auto fetch = [&](int j) {  // block of keys starting at j into the copy registers
+      if (j + BC <= T) {
+        ck.load(K + (size_t)j * rs, goff);
+        cv.load(V + (size_t)j * rs, goff);
+      } else {
+        ck.load_clamped(K, rs, j, T, tid);
+        cv.load_clamped(V, rs, j, T, tid);
       }
-      if (PREC == 0) {
+    };
+    fetch(0);
+    ck.store(sK[0], LD, tid);
+    cv.store(sV[0], LD, tid);
+    __syncthreads();
+
+    // Mask and reference-max update (with rescale) for one sub-tile's raw
+    // scores s of the block at key j0.
+    auto softmax_max = [&](int u, f32x16* s, int j0, auto masked) {
+      if (decltype(masked)::value) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) pk[kt][st] = pack32(s[kt], st);
-      }
-    }
-    lrow = lrow * alpha + ls;
-    if (__any(grew)) {
+        for (int kt = 0; kt < NKT; ++kt) {
+          const int lim = vis[u] - (j0 + 32 * kt);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-    }
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8 bf = PREC == 0 ? pk[kt][st] : pack32(s[kt], st);
-        bf16x8 bl;
-        if (PREC == 1) bl = pack32_lo(s[kt], st);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8 af = ld_tr32(cV, LD, 32 * kt + 16 * st, 32 * dt, lane);
-          oacc[dt] = mma32(af, bf, oacc[dt]);
-          if (PREC == 1) oacc[dt] = mma32(af, bl, oacc[dt]);
+          for (int e = 0; e < 16; ++e)
+            if (8 * (e >> 2) + (e & 3) > lim) s[kt][e] = -INFINITY;
         }
       }
-  };
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int j0 = kb * BC;
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) {
-      ck.load(K, rs, j0 + BC, T, tid);
-      cv.load(V, rs, j0 + BC, T, tid);
-    }
-    if (!CAUSAL || j0 <= r0 + 31) {
-      const bool need_mask = (CAUSAL && (j0 + BC - 1 > r0)) || (j0 + BC > T);
-      if (need_mask)
-        block(sK[buf], sV[buf], j0, std::true_type{});
-      else
-        block(sK[buf], sV[buf], j0, std::false_type{});
-    }
-    if (kb + 1 < nkb) {
-      ck.store(sK[buf ^ 1], LD, tid);
-      cv.store(sV[buf ^ 1], LD, tid);
-    }
-    __syncthreads();
-  }
-
-  const float l = lrow + __shfl_xor(lrow, 32);
-  if (row < T) {
-    float* O = a.o + base + (size_t)row * rs;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+      float mx = tile_max(s[0]);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int kt = 1; kt < NKT; ++kt) mx = fmaxf(mx, tile_max(s[kt]));
+      const float mb = half_swap_max(mx) * c2;
+      const bool raise = mb > mref[u] + kRescaleSlack;
+      if (__any(raise)) {
+        const float mnew = raise ? mb : mref[u];
+        const float alpha = mref[u] == -INFINITY ? 0.f : fast_exp2(mref[u] - mnew);
+        mref[u] = mnew;
+        ls0[u] *= alpha;
+        ls1[u] *= alpha;
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        f32x4 v4 = {oacc[dt][4 * bb] * inv, oacc[dt][4 * bb + 1] * inv, oacc[dt][4 * bb + 2] * inv,
-                    oacc[dt][4 * bb + 3] * inv};
-        *reinterpret_cast<f32x4*>(O + 32 * dt + 8 * bb + 4 * h) = v4;
+        for (int dt = 0; dt < NDT; ++dt) oacc[u][dt] *= alpha;
       }
-    if (h == 0) a.lse[(size_t)bh * T + row] = l > 0.f ? (mrow + log2f(l)) * kLn2 : -INFINITY;
-  }
+    };
+    // P = exp2(s c2 - m) packed to bfloat16 (pk; the residual in pl for the
+    // split precision), row sums updated.
+    auto softmax_exp = [&](int u, f32x16* s, bf16x8 (*pk)[2], bf16x8 (*pl)[2]) {
+      const float muse = mref[u] == -INFINITY ? 0.f : mref[u];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kt][e] = fast_exp2(fmaf(s[kt][e], c2, -muse));
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          pk[kt][st] = pack32(s[kt], st);
+          if (PREC == 0) sum8(pk[kt][st], one2, ls0[u], ls1[u]);
+          if (PREC == 1) pl[kt][st] = pack32_lo(s[kt], st);
+        }
+        if (PREC == 1) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ((e & 1) ? ls1[u] : ls0[u]) += s[kt][e];
+        }
+      }
+    };
+
+    // One K/V block with compile-time sub-tile states: 0 = not visited,
+    // 1 = every key visible, 2 = element-wise mask (causal diagonal or the end
+    // of the sequence).
+    auto block = [&](const bf16_t* cK, const bf16_t* cV, int j0, auto sa, auto sb) {
+      constexpr int S0 = decltype(sa)::value, S1 = decltype(sb)::value;
+      constexpr bool live[2] = {S0 != 0, MS > 1 && S1 != 0};
+      f32x16 s[MS][NKT];
+#pragma unroll
+      for (int u = 0; u < MS; ++u)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) s[u][kt] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+          const bf16x8 kop = ld_row32(cK, LD, 32 * kt, 16 * ks, n, h);
+#pragma unroll
+          for (int u = 0; u < MS; ++u)
+            if (live[u]) s[u][kt] = mma32(kop, qf[u][ks], s[u][kt]);
+        }
+      if (live[0]) softmax_max(0, s[0], j0, std::integral_constant<bool, S0 == 2>{});
+      if constexpr (MS > 1)
+        if (live[1]) softmax_max(1, s[1], j0, std::integral_constant<bool, S1 == 2>{});
+      bf16x8 vop[NKT][2][NDT];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) vop[kt][st][dt] = ld_tr32(cV, LD, 32 * kt + 16 * st, 32 * dt, lane);
+#pragma unroll
+      for (int u = 0; u < MS; ++u) {
+        if (!live[u]) continue;
+        bf16x8 pk[NKT][2], pl[NKT][2];
+        softmax_exp(u, s[u], pk, pl);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              oacc[u][dt] = mma32(vop[kt][st][dt], pk[kt][st], oacc[u][dt]);
+              if (PREC == 1) oacc[u][dt] = mma32(vop[kt][st][dt], pl[kt][st], oacc[u][dt]);
+            }
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int j0 = kb * BC;
+      const int buf = kb & 1;
+      if (kb + 1 < nkb) fetch(j0 + BC);
+      int code = 0;
+#pragma unroll
+      for (int u = 0; u < MS; ++u) {
+        const int st = kb > lastb[u] ? 0 : (((CAUSAL && j0 + BC - 1 > r0[u]) || j0 + BC > T) ? 2 : 1);
+        code = 3 * code + st;
+      }
+      const bf16_t* cK = sK[buf];
+      const bf16_t* cV = sV[buf];
+      if constexpr (MS == 2) {
+        switch (code) {
+          case 4: block(cK, cV, j0, I1{}, I1{}); break;
+          case 7: block(cK, cV, j0, I2{}, I1{}); break;
+          case 1: block(cK, cV, j0, I0{}, I1{}); break;
+          case 2: block(cK, cV, j0, I0{}, I2{}); break;
+          case 5: block(cK, cV, j0, I1{}, I2{}); break;
+          case 8: block(cK, cV, j0, I2{}, I2{}); break;
+          case 3: block(cK, cV, j0, I1{}, I0{}); break;
+          case 6: block(cK, cV, j0, I2{}, I0{}); break;
+          default: break;
+        }
+      } else {
+        if (code == 1) block(cK, cV, j0, I1{}, I0{});
+        else if (code == 2) block(cK, cV, j0, I2{}, I0{});
+      }
+      if (kb + 1 < nkb) {
+        ck.store(sK[buf ^ 1], LD, tid);
+        cv.store(sV[buf ^ 1], LD, tid);
+      }
+      __syncthreads();
+    }
+
+#pragma unroll
+    for (int u = 0; u < MS; ++u) {
+      const int row = r0[u] + n;
+      const float l = half_swap_sum(ls0[u] + ls1[u]);
+      if (row < T) {
+        float* O = a.o + base + (size_t)row * rs;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            f32x4 v4 = {oacc[u][dt][4 * bb] * inv, oacc[u][dt][4 * bb + 1] * inv, oacc[u][dt][4 * bb + 2] * inv,
+                        oacc[u][dt][4 * bb + 3] * inv};
+            *reinterpret_cast<f32x4*>(O + 32 * dt + 8 * bb + 4 * h) = v4;
+          }
+        if (h == 0) a.lse[(size_t)bh * T + row] = l > 0.f ? (mref[u] + log2f(l)) * kLn2 : -INFINITY;
+      }
+    }
   }
 }
 

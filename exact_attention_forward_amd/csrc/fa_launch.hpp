@@ -16,7 +16,13 @@ struct TileCfg;
 // bfloat16 kernels use 32x32 tiles: NW waves of 32 rows each.  The block
 // sizes can be overridden at compile time for tuning sweeps.
 #ifndef FA_FWD_BC64
-#define FA_FWD_BC64 64
+#define FA_FWD_BC64 32
+#endif
+#ifndef FA_FWD_NW64
+#define FA_FWD_NW64 2
+#endif
+#ifndef FA_FWD_MS64
+#define FA_FWD_MS64 2
 #endif
 #ifndef FA_DQ_BC64
 #define FA_DQ_BC64 64
@@ -27,9 +33,11 @@ struct TileCfg;
 #ifndef FA_NW64
 #define FA_NW64 4
 #endif
+// FWD_MS: 32-row sub-tiles per wave in the forward (rows per workgroup = 32 NW MS).
 template <int HD>
 struct TileCfg32 {
-  static constexpr int FWD_NW = HD <= 64 ? FA_NW64 : 4, FWD_BC = HD <= 64 ? FA_FWD_BC64 : 64;
+  static constexpr int FWD_NW = HD <= 64 ? FA_FWD_NW64 : 4, FWD_BC = HD <= 64 ? FA_FWD_BC64 : 64;
+  static constexpr int FWD_MS = HD <= 64 ? FA_FWD_MS64 : 1;
   static constexpr int DQ_NW = HD <= 64 ? FA_NW64 : 4, DQ_BC = HD <= 64 ? FA_DQ_BC64 : 64;
   static constexpr int DKV_NW = HD <= 64 ? FA_NW64 : 4, DKV_BQ = HD <= 64 ? FA_DKV_BQ64 : 64;
 };
@@ -85,8 +93,9 @@ template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_fwd(const FwdArgs& a, hipStream_t s) {
   if constexpr (sizeof(TIn) == 2) {
     using C = TileCfg32<HD>;
-    auto* k = &fwd32_kernel<HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC>;
-    const long items = (long)((a.T + C::FWD_NW * 32 - 1) / (C::FWD_NW * 32)) * a.B * a.H;
+    auto* k = &fwd32_kernel<HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC, C::FWD_MS>;
+    constexpr int BR = C::FWD_NW * 32 * C::FWD_MS;
+    const long items = (long)((a.T + BR - 1) / BR) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::FWD_NW * 64, items)), dim3(C::FWD_NW * 64), 0, s, a);
     return launch_status();
   }

@@ -82,4 +82,41 @@ __device__ __forceinline__ bf16x8 ld_row_global32(const bf16_t* X, size_t ld, in
   return z;
 }
 
+
+// Global -> register -> LDS copy of a block of ROWS rows x HD bfloat16 columns
+// (row-major, leading dimension gld elements in global memory, LD in LDS).
+// The per-thread byte offsets are computed once, so a block load is one
+// scalar base pointer plus a 32-bit offset per vector.  load() needs all ROWS
+// rows present; load_clamped() repeats the last valid row past nrows (finite
+// data, so zero weights on those rows contribute exactly zero).
+template <int HD, int ROWS, int NT>
+struct TileStream {
+  static constexpr int VPR = HD / 8;  // 16-byte vectors per row
+  static constexpr int NV = ROWS * VPR;
+  static constexpr int PER = (NV + NT - 1) / NT;
+  static_assert(NV % NT == 0, "copy must divide evenly");
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t r[PER];
+
+  __device__ __forceinline__ static int vrow(int tid, int p) { return (tid + p * NT) / VPR; }
+  __device__ __forceinline__ static int vcol(int tid, int p) { return ((tid + p * NT) % VPR) * 8; }
+
+  // goff[p]: byte offset of vector p from the block's first row.
+  __device__ __forceinline__ void load(const bf16_t* G, const unsigned* goff) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) r[p] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(G) + goff[p]);
+  }
+  __device__ __forceinline__ void load_clamped(const bf16_t* G, size_t gld, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int gr = min(row0 + vrow(tid, p), nrows - 1);
+      r[p] = *reinterpret_cast<const u32x4_t*>(G + (size_t)gr * gld + vcol(tid, p));
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* S, int ld, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) *reinterpret_cast<u32x4_t*>(S + vrow(tid, p) * ld + vcol(tid, p)) = r[p];
+  }
+};
+
 }  // namespace fa
