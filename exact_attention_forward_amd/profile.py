@@ -1,0 +1,244 @@
+"""Summaries of rocprofv3 results for the attention kernels (host-side tool).
+
+Reads the SQLite result databases rocprofv3 writes (``-d DIR -o NAME``) and
+prints or writes short Markdown summaries plus ``traffic.json``:
+
+* ``trace``: per-kernel call count, total and mean duration from a
+  ``--kernel-trace --stats`` run;
+* ``traffic``: HBM bytes per launch from a ``--pmc FETCH_SIZE`` run and a
+  ``--pmc WRITE_SIZE`` run of ``bench.py --counters``, each scaled by what the
+  same counter reads for the plain device copy of known size that
+  ``bench.py --counters`` runs first (``__amd_rocclr_copyBuffer``);
+* ``util``: the derived metrics MfmaUtil, VALUBusy, LDSBankConflict and
+  OccupancyPercent, plus executed bf16 matrix operations.
+
+Usage (from the repository root, on the machine where the databases are)::
+
+    python -m exact_attention_forward_amd.profile trace  DB
+    python -m exact_attention_forward_amd.profile traffic FETCH_DB WRITE_DB
+    python -m exact_attention_forward_amd.profile util DB
+    python -m exact_attention_forward_amd.profile report TRACE_DB FETCH_DB WRITE_DB UTIL_DB OUT_DIR HASH
+
+``report`` writes the Markdown summaries and ``traffic.json`` of the causal
+B64 H16 T1024 hd64 bfloat16 workload into OUT_DIR; HASH is the kernel source
+hash bench.py prints for the build that was profiled (bench.py reports the
+measured traffic only while the sources still hash to it).
+
+The counter values are per dispatch (already reduced over hardware instances
+by rocprofv3); a kernel launched several times is averaged over its launches.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import json
+import sqlite3
+import sys
+from pathlib import Path
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+ATTN_KERNELS = ("fwd32_kernel", "dq32_kernel", "dkv32_kernel", "fwd_kernel", "dq_kernel", "dkv_kernel",
+                "delta_kernel")
+
+
+def short_name(k: str) -> str:
+    s = k.split("(")[0]
+    for p in ("void ", "fa::"):
+        s = s.replace(p, "")
+    return s.strip()
+
+
+def family(k: str) -> str | None:
+    s = short_name(k)
+    for f in ATTN_KERNELS:
+        if s.startswith(f + "<") or s == f:
+            return f
+    return None
+
+
+def kernel_durations(db: str) -> dict:
+    """Kernel name -> list of dispatch durations (ns)."""
+    c = sqlite3.connect(db)
+    out = collections.defaultdict(list)
+    for name, dur in c.execute("select name, duration from kernels"):
+        out[name].append(float(dur))
+    return out
+
+
+def counters(db: str) -> dict:
+    """Kernel name -> counter -> list of per-dispatch values."""
+    c = sqlite3.connect(db)
+    per = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    for name, dis, cn, v in c.execute("select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+        per[name][cn][dis] += float(v)
+    return {k: {cn: list(d.values()) for cn, d in v.items()} for k, v in per.items()}
+
+
+def mean(x):
+    return sum(x) / len(x) if x else float("nan")
+
+
+def trace_table(db: str) -> str:
+    d = kernel_durations(db)
+    rows = [(k, len(v), sum(v) / 1e3, mean(v) / 1e3) for k, v in d.items() if family(k)]
+    tot = sum(r[2] for r in rows)
+    lines = ["| kernel | calls | total us | avg us | share % |", "|---|---|---|---|---|"]
+    for k, n, t, a in sorted(rows, key=lambda r: -r[2]):
+        lines.append(f"| `{short_name(k)}` | {n} | {t:.1f} | {a:.2f} | {100 * t / tot:.1f} |")
+    return "\n".join(lines)
+
+
+def traffic(fetch_db: str, write_db: str) -> dict:
+    f, w = counters(fetch_db), counters(write_db)
+
+    def copy_kib(cs, cn):
+        for k, v in cs.items():
+            if COPY_KERNEL in k and cn in v:
+                return max(v[cn])
+        raise RuntimeError(f"no {COPY_KERNEL} dispatch with {cn}")
+
+    copy_bytes = 1 << 30
+    rscale = copy_bytes / 1024 / copy_kib(f, "FETCH_SIZE")
+    wscale = copy_bytes / 1024 / copy_kib(w, "WRITE_SIZE")
+    kern = {}
+    for k in set(f) | set(w):
+        fam = family(k)
+        if fam is None:
+            continue
+        fk = mean(f.get(k, {}).get("FETCH_SIZE", []))
+        wk = mean(w.get(k, {}).get("WRITE_SIZE", []))
+        kern[fam] = {"kernel": short_name(k), "fetch_kib": fk, "write_kib": wk,
+                     "hbm_read_bytes": int(fk * 1024 * rscale), "hbm_write_bytes": int(wk * 1024 * wscale)}
+        kern[fam]["hbm_bytes_per_launch"] = kern[fam]["hbm_read_bytes"] + kern[fam]["hbm_write_bytes"]
+    return {"read_scale": rscale, "write_scale": wscale, "copy_fetch_kib": copy_kib(f, "FETCH_SIZE"),
+            "copy_write_kib": copy_kib(w, "WRITE_SIZE"), "kernels": kern}
+
+
+def util(db: str) -> dict:
+    cs = counters(db)
+    out = {}
+    for k, v in cs.items():
+        fam = family(k)
+        if fam is None:
+            continue
+        out[fam] = {"kernel": short_name(k), **{cn: mean(vals) for cn, vals in v.items()}}
+    return out
+
+
+# ---- closed forms for the report (causal B64 H16 T1024 hd64, bf16 inputs) ----
+# Fused-kernel request counts in the style of the fused-attention facts page
+# (block "traffic"): one head, N rows of width d, query tiles of Br rows, G of
+# them.  Non-causal: reads N d + 2 G N d elements, writes N d.  The causal
+# kernel visits, for query tile t, the keys 0 .. (t + 1) Br - 1 only.
+def fused_requests(N: int, d: int, Br: int, causal: bool) -> dict:
+    G = -(-N // Br)
+    if causal:
+        kv_keys = sum(min((t + 1) * Br, N) for t in range(G))
+    else:
+        kv_keys = G * N
+    return {"G": G, "reads": N * d + 2 * kv_keys * d, "writes": N * d}
+
+
+def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
+           B=64, H=16, T=1024, hd=64, fwd_rows=128) -> None:
+    out = Path(out_dir)
+    heads = B * H
+    d = kernel_durations(trace_db)
+    avg_us = {family(k): mean(v) / 1e3 for k, v in d.items() if family(k)}
+    tr = traffic(fetch_db, write_db)
+    ut = util(util_db)
+    tr_json = {"workload": f"causal attention fwd+bwd B{B} H{H} T{T} hd{hd} bf16", "kernel_source_hash": src_hash,
+               "read_scale": tr["read_scale"], "write_scale": tr["write_scale"],
+               "kernels": {k: {kk: v[kk] for kk in ("kernel", "hbm_read_bytes", "hbm_write_bytes",
+                                                    "hbm_bytes_per_launch")} for k, v in tr["kernels"].items()}}
+    (out / "traffic.json").write_text(json.dumps(tr_json, indent=1) + "\n")
+
+    # compulsory bytes per launch: every tensor once (bf16 inputs, f32 O / L / D / grads)
+    E, nd = heads * T * hd, heads * T
+    comp = {"fwd32_kernel": (3 * 2 * E, 4 * E + 4 * nd),
+            "dq32_kernel": (4 * 2 * E + 4 * E + 4 * nd, 4 * E + 4 * nd),
+            "dkv32_kernel": (4 * 2 * E + 8 * nd, 8 * E)}
+    fr = fused_requests(T, hd, fwd_rows, True)
+    fr_nc = fused_requests(T, hd, fwd_rows, False)
+    lines = [f"# HBM traffic per launch: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
+             "Commands (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, paths absolute):",
+             "", "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch -- python3 bench.py --counters",
+             "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write -- python3 bench.py --counters",
+             "    python -m exact_attention_forward_amd.profile report ...", "",
+             f"Calibration: the same counters on a plain device copy of 1 GiB (`{COPY_KERNEL}`) read FETCH_SIZE "
+             f"{tr['copy_fetch_kib']:.1f} KiB and WRITE_SIZE {tr['copy_write_kib']:.1f} KiB for 1048576 KiB moved each "
+             f"way, so reads are scaled by {tr['read_scale']:.4f} and writes by {tr['write_scale']:.4f}.", "",
+             "| kernel | avg us | HBM read MB | HBM write MB | HBM GB/s | % of 8 TB/s | read / compulsory | write / compulsory |",
+             "|---|---|---|---|---|---|---|---|"]
+    for fam in ("fwd32_kernel", "dq32_kernel", "dkv32_kernel"):
+        if fam not in tr["kernels"]:
+            continue
+        k = tr["kernels"][fam]
+        t_us = avg_us.get(fam, float("nan"))
+        gbs = k["hbm_bytes_per_launch"] / (t_us * 1e-6) / 1e9
+        cr, cw = comp[fam]
+        lines.append(f"| `{k['kernel']}` | {t_us:.1f} | {k['hbm_read_bytes'] / 1e6:.1f} | {k['hbm_write_bytes'] / 1e6:.1f} "
+                     f"| {gbs:.0f} | {100 * gbs / 8000:.1f} | {k['hbm_read_bytes'] / cr:.2f} | {k['hbm_write_bytes'] / cw:.2f} |")
+    fwd = tr["kernels"].get("fwd32_kernel")
+    lines += ["", "Forward against the closed form of the fused-attention facts page (block `traffic`), per head, "
+              f"N = {T}, d = {hd}, query tiles of {fwd_rows} rows (G = {fr['G']}), counted in elements:", "",
+              f"* page form, no mask: reads N d + 2 G N d = {fr_nc['reads']}, writes N d = {fr_nc['writes']};",
+              f"* the same count for the causal walk (query tile t reads keys below (t + 1) {fwd_rows}): "
+              f"reads {fr['reads']}, writes {fr['writes']};"]
+    if fwd:
+        per_head_r = fwd["hbm_read_bytes"] / heads / 2  # bf16 elements
+        lines += [f"* measured HBM reads per head: {per_head_r:.0f} bf16 elements = "
+                  f"{per_head_r / fr['reads']:.2f} of the causal request count and "
+                  f"{per_head_r / (3 * T * hd):.2f} of reading Q, K, V once; the repeated K/V tile reads of later query "
+                  "tiles are served by L2, so HBM traffic stays linear in N."]
+    (out / f"hbm_traffic_gpt2m_bf16.md").write_text("\n".join(lines) + "\n")
+
+    lines = [f"# Kernel trace: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
+             "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, paths absolute):",
+             "", "    rocprofv3 --kernel-trace --stats -d gpurun_out/prof_trace -o trace -- "
+             "python3 bench.py --no-cpu-baseline --steps 20 --warmup 5", "", trace_table(trace_db)]
+    (out / "kernel_trace_gpt2m_bf16.md").write_text("\n".join(lines) + "\n")
+
+    flops = {"fwd32_kernel": 4, "dq32_kernel": 6, "dkv32_kernel": 8}
+    pairs = heads * T * T / 2
+    lines = [f"# Matrix-core and vector-ALU use: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
+             "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, paths absolute):", "",
+             "    rocprofv3 --pmc MfmaUtil VALUBusy LDSBankConflict OccupancyPercent SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+             "-d gpurun_out/prof_util -o util -- python3 bench.py --counters", "",
+             "MfmaUtil = busy cycles of the matrix cores over (GPU-active cycles x SIMDs); executed bf16 matrix flops = "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; algorithmic flops count hd-long products per visible (query, key) pair "
+             "(forward 4 hd, dQ kernel 6 hd, dK/dV kernel 8 hd; B H T^2 / 2 pairs).", "",
+             "| kernel | avg us | MfmaUtil % | VALUBusy % | LDSBankConflict % | OccupancyPercent % | executed GFLOP | "
+             "algorithmic GFLOP | algorithmic TFLOP/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for fam in ("fwd32_kernel", "dq32_kernel", "dkv32_kernel"):
+        if fam not in ut:
+            continue
+        u = ut[fam]
+        t_us = avg_us.get(fam, float("nan"))
+        alg = flops[fam] * hd * pairs
+        lines.append(f"| `{u['kernel']}` | {t_us:.1f} | {u.get('MfmaUtil', float('nan')):.1f} | "
+                     f"{u.get('VALUBusy', float('nan')):.1f} | {u.get('LDSBankConflict', float('nan')):.1f} | "
+                     f"{u.get('OccupancyPercent', float('nan')):.1f} | "
+                     f"{u.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', float('nan')) * 512 / 1e9:.1f} | {alg / 1e9:.1f} | "
+                     f"{alg / (t_us * 1e-6) / 1e12:.0f} |")
+    (out / "mfma_util_gpt2m_bf16.md").write_text("\n".join(lines) + "\n")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("what", choices=("trace", "traffic", "util", "report"))
+    ap.add_argument("db", nargs="+")
+    a = ap.parse_args(argv)
+    if a.what == "trace":
+        print(trace_table(a.db[0]))
+    elif a.what == "traffic":
+        print(json.dumps(traffic(a.db[0], a.db[1]), indent=1))
+    elif a.what == "util":
+        print(json.dumps(util(a.db[0]), indent=1))
+    else:
+        report(*a.db[:6])
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
