@@ -22,6 +22,16 @@ GPU outputs with it.
 
 ``--counters`` runs a minimal program for rocprofv3 --pmc: a float32 copy of
 known size (the calibration kernel), then a few steps.
+
+``--lab`` runs the lab of the fused-attention lesson instead: one head, no
+mask, float32 inputs uniform in [-2, 2), N in {256, ..., 4096}, d in {16, 64};
+for the fused forward, the unfused three-kernel forward and the no-rescale
+control it times 9 runs after one warm-up (HIP events around each run, the
+unfused kernels' three dispatches in one timed run) and prints one JSON line
+with the median milliseconds and the unfused/fused ratio.  Parity of these
+kernels against the float64 reference with the lesson's error bound is checked
+by tests/test_gpu_lab.py.  ``--lab --counters`` instead runs the calibration
+copy and then each (N, d, kind) once, for rocprofv3 --pmc.
 """
 from __future__ import annotations
 
@@ -73,6 +83,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="minimal run for rocprofv3 counter collection")
+    ap.add_argument("--lab", action="store_true", help="fused vs unfused lab of the lesson (one head, float32)")
     return ap.parse_args()
 
 
@@ -88,6 +99,9 @@ def main() -> int:
 
     import exact_attention_forward_amd as fa
     from exact_attention_forward_amd import inputs as I
+
+    if args.lab:
+        return lab(args)
 
     case = I.gpt2m_case(I.BF16)
     B, H, T, hd = case.B, case.H, case.T, case.hd
@@ -173,6 +187,63 @@ def main() -> int:
         rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(case, dict(O=o, L=lse, dQ=dq, dK=dk, dV=dv),
                                                                  args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+    return 0
+
+
+def lab(args) -> int:
+    """Median times of the fused, unfused and no-rescale forwards over the lesson's lab grid."""
+    import torch
+
+    import exact_attention_forward_amd as fa
+    from exact_attention_forward_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    if args.counters:
+        x = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+    rows = []
+    for d in I.LAB_WIDTHS:
+        for N in I.LAB_SIZES:
+            c = I.lab_case(N, d)
+            q, k, v = (torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v"))
+            o = torch.empty((1, N, 1, d), device=dev)
+            lse = torch.empty((1, 1, N), device=dev)
+            s = torch.empty((1, 1, N, N), device=dev)
+            runs = {
+                "fused": lambda: fa.check(fa.fa_forward(q, k, v, o, lse, 1, 1, N, d, c.scale, 0, fa.FA_F32, 0, stream)),
+                "unfused": lambda: fa.check(fa.fa_forward_unfused(q, k, v, o, s, 1, 1, N, d, c.scale, 0, fa.FA_F32,
+                                                                  stream)),
+                "broken": lambda: fa.check(fa.fa_forward_norescale(q, k, v, o, lse, 1, 1, N, d, c.scale, 0, fa.FA_F32,
+                                                                   stream)),
+            }
+            row = {"N": N, "d": d}
+            for kind, fn in runs.items():
+                if args.counters:
+                    fn()
+                    torch.cuda.synchronize()
+                    continue
+                fn()  # warm-up
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(9):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1))
+                row[kind + "_ms"] = round(sorted(ts)[len(ts) // 2], 5)
+            if not args.counters:
+                row["unfused_over_fused"] = round(row["unfused_ms"] / row["fused_ms"], 3)
+                row["score_bytes_saved"] = 16 * N * N
+            rows.append(row)
+    print(json.dumps({"lab": "fused vs unfused attention forward, one head, no mask, float32", "reps": 9,
+                      "warmup": 1, "statistic": "median ms (HIP events)", "device": torch.cuda.get_device_name(dev),
+                      "rows": rows} if not args.counters else {"lab_counters_run": "done"}), flush=True)
     return 0
 
 

@@ -35,6 +35,8 @@ SIGNATURES = {
     "fa_backward_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_backward_dkv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_backward_dq_delta": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_forward_unfused": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_forward_norescale": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_is_supported": (_I, [_I, _I]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -93,6 +95,16 @@ def check(status: int) -> None:
 def fa_forward(q, k, v, o, lse, B, H, T, hd, scale, causal, dtype, prec, stream) -> int:
     return lib().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, T, hd, scale, int(causal), dtype,
                             prec, _stream(stream))
+
+
+def fa_forward_unfused(q, k, v, o, scores, B, H, T, hd, scale, causal, dtype, stream) -> int:
+    return lib().fa_forward_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(scores), B, H, T, hd, scale, int(causal),
+                                    dtype, _stream(stream))
+
+
+def fa_forward_norescale(q, k, v, o, lse, B, H, T, hd, scale, causal, dtype, stream) -> int:
+    return lib().fa_forward_norescale(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, T, hd, scale, int(causal),
+                                      dtype, _stream(stream))
 
 
 def fa_backward(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, T, hd, scale, causal, dtype, prec, stream) -> int:

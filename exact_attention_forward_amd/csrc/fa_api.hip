@@ -107,6 +107,40 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
   return run(fa::kFwd, hd, dtype, prec, causal != 0, &a, stream);
 }
 
+int fa_forward_norescale(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T,
+                         int hd, float scale, int causal, fa_dtype dtype, void* stream) {
+  int st = check_common(B, H, T, hd, dtype, FA_PREC_DEFAULT);
+  if (st) return st;
+  if (dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale, causal))) return st;
+  const void* ptrs[] = {q, k, v, o, lse};
+  if ((st = check_ptrs(ptrs, 5))) return st;
+  const size_t n = (size_t)B * T * H * hd;
+  const Buf in[] = {{q, n * 4}, {k, n * 4}, {v, n * 4}};
+  const Buf out[] = {{o, n * 4}, {lse, (size_t)B * H * T * 4}};
+  if ((st = check_alias(in, 3, out, 2))) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, T, log2e_scaled(scale)};
+  return run(fa::kFwdNoRescale, hd, dtype, FA_PREC_DEFAULT, causal != 0, &a, stream);
+}
+
+int fa_forward_unfused(const void* q, const void* k, const void* v, float* o, float* scores, int B, int H, int T,
+                       int hd, float scale, int causal, fa_dtype dtype, void* stream) {
+  int st = check_common(B, H, T, hd, dtype, FA_PREC_DEFAULT);
+  if (st) return st;
+  if (dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale, causal))) return st;
+  if ((double)B * H > 65535.0 || (double)B * H * T * T >= 1099511627776.0) return FA_ERR_ARG;
+  const void* ptrs[] = {q, k, v, o, scores};
+  if ((st = check_ptrs(ptrs, 5))) return st;
+  const size_t n = (size_t)B * T * H * hd;
+  const Buf in[] = {{q, n * 4}, {k, n * 4}, {v, n * 4}};
+  const Buf out[] = {{o, n * 4}, {scores, (size_t)B * H * T * T * 4}};
+  if ((st = check_alias(in, 3, out, 2))) return st;
+  fa::UnfusedArgs a{static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), o,
+                    scores, B, H, T, scale};
+  return fa::unfused_f32(hd, a, causal != 0, static_cast<hipStream_t>(stream));
+}
+
 int fa_backward_delta(const float* o, const void* dO, float* delta, int B, int H, int T, int hd, fa_dtype dtype,
                       void* stream) {
   int st = check_common(B, H, T, hd, dtype, FA_PREC_DEFAULT);

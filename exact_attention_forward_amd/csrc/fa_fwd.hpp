@@ -39,7 +39,12 @@ struct FwdArgs {
 
 // PREC: 0 = operands rounded to bfloat16 (or exact f32), 1 = P split into a
 // bfloat16 high part and a bfloat16 residual (two products).
-template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int MR, int BC>
+// NORESCALE: the control variant of the fused-attention lesson (blocks
+// "controls" and "correctness"): when a row's running max rises, the running
+// sum l and the accumulated output are NOT multiplied by alpha.  The result is
+// wrong whenever a later key block raises a row's max; it exists only so that
+// the error checker can be shown to catch it.
+template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int MR, int BC, bool NORESCALE = false>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   using M = Mma<TIn>;
   using frag = typename M::frag;
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         mx = group_max(mx);
         const float mold = mrow[mr];
         const float mnew = fmaxf(mold, mx * c2);
-        const float alpha = (mold == -INFINITY) ? 0.f : fast_exp2(mold - mnew);
+        const float alpha = NORESCALE ? 1.f : ((mold == -INFINITY) ? 0.f : fast_exp2(mold - mnew));
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
         mrow[mr] = mnew;
         float ls = 0.f;

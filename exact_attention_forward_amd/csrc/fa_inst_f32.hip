@@ -25,4 +25,15 @@ int delta_f32(int hd, const BwdArgs& a, hipStream_t s) {
   }
 }
 
+int unfused_f32(int hd, const UnfusedArgs& a, bool causal, hipStream_t s) {
+  switch (hd) {
+    case 8: return run_unfused<8>(a, causal, s);
+    case 16: return run_unfused<16>(a, causal, s);
+    case 32: return run_unfused<32>(a, causal, s);
+    case 64: return run_unfused<64>(a, causal, s);
+    case 128: return run_unfused<128>(a, causal, s);
+    default: return -3;
+  }
+}
+
 }  // namespace fa

@@ -5,6 +5,7 @@
 #include "fa_bwd32.hpp"
 #include "fa_fwd.hpp"
 #include "fa_fwd32.hpp"
+#include "fa_unfused.hpp"
 
 namespace fa {
 
@@ -89,23 +90,26 @@ inline long persistent_grid(K kernel, int threads, long items) {
   return items < slots ? items : slots;
 }
 
-template <typename TIn, int HD, bool CAUSAL, int PREC>
+template <typename TIn, int HD, bool CAUSAL, int PREC, bool NORESCALE = false>
 int run_fwd(const FwdArgs& a, hipStream_t s) {
-  if constexpr (sizeof(TIn) == 2) {
+  if constexpr (NORESCALE && sizeof(TIn) == 2) {
+    return -3;  // the control variant is built for float32 inputs only
+  } else if constexpr (sizeof(TIn) == 2) {
     using C = TileCfg32<HD>;
     auto* k = &fwd32_kernel<HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC, C::FWD_MS>;
     constexpr int BR = C::FWD_NW * 32 * C::FWD_MS;
     const long items = (long)((a.T + BR - 1) / BR) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::FWD_NW * 64, items)), dim3(C::FWD_NW * 64), 0, s, a);
     return launch_status();
+  } else {
+    using C = TileCfg<TIn, HD>;
+    constexpr int BR = C::FWD_NW * 16 * C::FWD_MR;
+    const long nqt = (a.T + BR - 1) / BR;
+    const long grid = nqt * a.B * a.H;
+    hipLaunchKernelGGL((fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC, NORESCALE>),
+                       dim3((unsigned)grid), dim3(C::FWD_NW * 64), 0, s, a);
+    return launch_status();
   }
-  using C = TileCfg<TIn, HD>;
-  constexpr int BR = C::FWD_NW * 16 * C::FWD_MR;
-  const long nqt = (a.T + BR - 1) / BR;
-  const long grid = nqt * a.B * a.H;
-  hipLaunchKernelGGL((fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC>), dim3((unsigned)grid),
-                     dim3(C::FWD_NW * 64), 0, s, a);
-  return launch_status();
 }
 
 template <typename TIn, int HD>
@@ -154,12 +158,13 @@ int run_dkv(const BwdArgs& a, hipStream_t s) {
   return launch_status();
 }
 
-enum Stage { kFwd = 0, kDq = 1, kDkv = 2, kDqDelta = 3 };
+enum Stage { kFwd = 0, kDq = 1, kDkv = 2, kDqDelta = 3, kFwdNoRescale = 4 };
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_stage(int stage, const void* args, hipStream_t s) {
   switch (stage) {
     case kFwd: return run_fwd<TIn, HD, CAUSAL, PREC>(*static_cast<const FwdArgs*>(args), s);
+    case kFwdNoRescale: return run_fwd<TIn, HD, CAUSAL, PREC, true>(*static_cast<const FwdArgs*>(args), s);
     case kDq: return run_dq<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);
     case kDqDelta: return run_dq<TIn, HD, CAUSAL, PREC, true>(*static_cast<const BwdArgs*>(args), s);
     default: return run_dkv<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);
@@ -180,6 +185,7 @@ int run_stage_hd(int stage, const void* args, bool causal, int prec, hipStream_t
 int stage_f32(int stage, int hd, const void* args, bool causal, hipStream_t s);
 int stage_bf16(int stage, int hd, const void* args, bool causal, int prec, hipStream_t s);
 int delta_f32(int hd, const BwdArgs& a, hipStream_t s);
+int unfused_f32(int hd, const UnfusedArgs& a, bool causal, hipStream_t s);
 int delta_bf16(int hd, const BwdArgs& a, hipStream_t s);
 
 }  // namespace fa

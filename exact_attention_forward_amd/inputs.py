@@ -132,3 +132,17 @@ LONG = dict(B=4, H=16, T=8192, hd=128)
 def long_case() -> Case:
     """Long-context causal attention (B4 H16 T8192 hd128), bfloat16, seed 4, 1% of key rows x8."""
     return make_case("long_bf16", LONG["B"], LONG["H"], LONG["T"], LONG["hd"], BF16, True, 4, outlier_frac=0.01)
+
+
+# The lab of the fused-attention lesson: one head, no mask, float32, inputs
+# uniform in [-2, 2) (the lesson's correctness inputs), scale 1/sqrt(d).
+LAB_SIZES = (256, 512, 1024, 2048, 4096)
+LAB_WIDTHS = (16, 64)
+
+
+def lab_case(N: int, d: int, seed: int = 1) -> Case:
+    """One head of N rows of width d: q, k, v uniform in [-2, 2) drawn in that order, float32."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.uniform(-2.0, 2.0, (1, N, 1, d)).astype(np.float32) for _ in range(3))
+    do = np.zeros_like(q)
+    return Case(f"lab_N{N}_d{d}", 1, 1, N, d, F32, False, 1.0 / math.sqrt(d), seed, q, k, v, do)

@@ -75,6 +75,38 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
                float scale, int causal, fa_dtype dtype, fa_precision prec, void* stream);
 
 /*
+ * Unfused forward (float32 inputs only), the comparator of the fused-attention
+ * lesson ("Lesson K23, fused attention", blocks "sources" -- Algorithm 0 of
+ * the FlashAttention paper -- and "lab"): three kernels in order on `stream`,
+ * a scores kernel writing S = scale * q k^T to `scores`, a row softmax
+ * kernel overwriting S with P (masked keys get P = 0), and a kernel writing
+ * o = P v.  The score matrix makes 4 T^2 floats per head of extra global
+ * traffic against fa_forward.  No lse is produced.
+ *   q, k, v   [B, T, H, hd] float32 inputs
+ *   o         [B, T, H, hd] float32 output
+ *   scores    [B, H, T, T] float32 caller-provided workspace; on return it
+ *             holds P
+ * Extra limits: B * H <= 65535 and B * H * T * T < 2^40.  Returns
+ * FA_ERR_UNSUPPORTED for bfloat16 inputs.
+ */
+int fa_forward_unfused(const void* q, const void* k, const void* v, float* o, float* scores, int B, int H, int T,
+                       int hd, float scale, int causal, fa_dtype dtype, void* stream);
+
+/*
+ * Control variant of fa_forward (float32 inputs only), deliberately WRONG:
+ * when a key block raises a row's running max, the running sum l and the
+ * accumulated output are not rescaled by alpha = exp(m_old - m_new) (the
+ * "broken" kernel of the fused-attention lesson, blocks "controls" and
+ * "correctness"; the rescale is step 3 of "Loop (per (b, h, Q-tile))" in the
+ * forward notes).  It agrees with fa_forward only while every row's max is
+ * set by its first key block (T <= 32 keys here), and exists so that error
+ * checkers can be shown to reject it.  Same arguments and contract as
+ * fa_forward (precision FA_PREC_DEFAULT); FA_ERR_UNSUPPORTED for bfloat16.
+ */
+int fa_forward_norescale(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T,
+                         int hd, float scale, int causal, fa_dtype dtype, void* stream);
+
+/*
  * Backward pass with recomputation (backward notes, "The math (FA2 backward
  * with recompute)"): from the forward's o and lse and the upstream gradient
  * dO = d loss / d o, writes dq, dk, dv.  Runs fa_backward_dq_delta, then

@@ -97,24 +97,28 @@ def finish(st):
     return o / l, m + math.log(l)
 
 
-def tiled_forward(q, k, v, scale: float, causal: bool, br: int, bc: int, rescale: bool = True):
+def tiled_forward(q, k, v, scale: float, causal: bool, br: int, bc: int, rescale: bool = True,
+                  dtype=np.float64):
     """One head, q/k/v [T, hd]; query tiles of br rows, key blocks of bc rows.
 
     Returns (O [T, hd], L [T]).  Rows past T in a tile and keys past T in a
     block are excluded; in causal mode key j is visible to row i iff j <= i.
+    ``dtype=np.float32`` runs every step in float32 (the tiled float32 output
+    the lesson's checker control must accept).
     """
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
+    q = np.asarray(q, dtype)
+    k = np.asarray(k, dtype)
+    v = np.asarray(v, dtype)
+    scale = dtype(scale)
     T, hd = q.shape
-    O = np.zeros((T, hd))
-    L = np.zeros(T)
+    O = np.zeros((T, hd), dtype)
+    L = np.zeros(T, dtype)
     for i0 in range(0, T, br):
         rows = range(i0, min(i0 + br, T))
         last = rows[-1]
-        m = np.full(len(rows), -np.inf)
-        l = np.zeros(len(rows))
-        o = np.zeros((len(rows), hd))
+        m = np.full(len(rows), -np.inf, dtype)
+        l = np.zeros(len(rows), dtype)
+        o = np.zeros((len(rows), hd), dtype)
         for j0 in range(0, T, bc):
             if causal and j0 > last:
                 break  # every later block is wholly above the diagonal
@@ -125,10 +129,11 @@ def tiled_forward(q, k, v, scale: float, causal: bool, br: int, bc: int, rescale
             mb = s.max(axis=1)
             mn = np.maximum(m, mb)
             if rescale:
-                alpha = np.where(m == -np.inf, 0.0, np.exp(m - mn))
+                alpha = np.where(m == -np.inf, dtype(0), np.exp(m - mn)).astype(dtype)
             else:
                 alpha = np.ones_like(m)
-            p = np.where(np.isneginf(s), 0.0, np.exp(s - np.where(np.isneginf(mn), 0.0, mn)[:, None]))
+            p = np.where(np.isneginf(s), dtype(0), np.exp(s - np.where(np.isneginf(mn), dtype(0), mn)[:, None]))
+            p = p.astype(dtype)
             l = l * alpha + p.sum(axis=1)
             o = o * alpha[:, None] + p @ v[cols]
             m = mn

@@ -131,3 +131,26 @@ def test_stage_entry_points_validate(lib):
                               None) == fa.FA_ERR_ALIAS
     assert fa.fa_backward_dkv(P[0], P[1], P[2], P[4], P[5], P[9], P[7], P[8], 1, 2, 8, 64, 0.1, 0, fa.FA_BF16, 3,
                               None) == fa.FA_ERR_ARG
+
+
+def test_unfused_and_control_entry_points_validate(lib):
+    # float32 only
+    assert fa.fa_forward_unfused(P[0], P[1], P[2], P[3], P[4], 1, 2, 8, 64, 0.1, 0, fa.FA_BF16, None) == \
+        fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_forward_norescale(P[0], P[1], P[2], P[3], P[4], 1, 2, 8, 64, 0.1, 0, fa.FA_BF16, None) == \
+        fa.FA_ERR_UNSUPPORTED
+    # the score workspace is an output: it may not overlap an input or o
+    assert fa.fa_forward_unfused(P[0], P[1], P[2], P[3], P[2], 1, 2, 8, 64, 0.1, 0, fa.FA_F32, None) == fa.FA_ERR_ALIAS
+    assert fa.fa_forward_unfused(P[0], P[1], P[2], P[3], P[3] + 64, 1, 2, 8, 64, 0.1, 0, fa.FA_F32, None) == \
+        fa.FA_ERR_ALIAS
+    assert fa.fa_forward_unfused(P[0], P[1], P[2], P[3], None, 1, 2, 8, 64, 0.1, 0, fa.FA_F32, None) == fa.FA_ERR_ARG
+    assert fa.fa_forward_unfused(P[0], P[1], P[2], P[3], P[4] + 4, 1, 2, 8, 64, 0.1, 0, fa.FA_F32, None) == \
+        fa.FA_ERR_ALIGN
+    assert fa.fa_forward_unfused(P[0], P[1], P[2], P[3], P[4], 1, 1 << 16, 8, 64, 0.1, 0, fa.FA_F32, None) == \
+        fa.FA_ERR_ARG  # B * H above 65535
+    assert fa.fa_forward_unfused(P[0], P[1], P[2], P[3], P[4], 1, 2, 8, 96, 0.1, 0, fa.FA_F32, None) == \
+        fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_forward_norescale(P[0], P[1], P[2], P[3], P[4], 1, 2, 8, 64, -1.0, 0, fa.FA_F32, None) == \
+        fa.FA_ERR_ARG
+    assert fa.fa_forward_norescale(P[0], P[1], P[2], P[0], P[4], 1, 2, 8, 64, 0.1, 0, fa.FA_F32, None) == \
+        fa.FA_ERR_ALIAS
