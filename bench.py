@@ -25,8 +25,9 @@ known size (the calibration kernel), then a few steps.
 
 ``--lab`` runs the lab of the fused-attention lesson instead: one head, no
 mask, float32 inputs uniform in [-2, 2), N in {256, ..., 4096}, d in {16, 64};
-for the fused forward, the unfused three-kernel forward and the no-rescale
-control it times 9 runs after one warm-up (HIP events around each run, the
+for the fused forward, the unfused three-kernel forward, the no-rescale
+control and the split-key forward (128 keys per split) it times 9 runs after
+one warm-up (HIP events around each run, the
 unfused kernels' three dispatches in one timed run) and prints one JSON line
 with the median milliseconds and the unfused/fused ratio.  Parity of these
 kernels against the float64 reference with the lesson's error bound is checked
@@ -213,14 +214,18 @@ def lab(args) -> int:
             o = torch.empty((1, N, 1, d), device=dev)
             lse = torch.empty((1, 1, N), device=dev)
             s = torch.empty((1, 1, N, N), device=dev)
+            nsplit = min(64, max(1, N // 128))  # 128 keys per split
+            ws = torch.empty((nsplit * (N * d + N),), device=dev)
             runs = {
                 "fused": lambda: fa.check(fa.fa_forward(q, k, v, o, lse, 1, 1, N, d, c.scale, 0, fa.FA_F32, 0, stream)),
                 "unfused": lambda: fa.check(fa.fa_forward_unfused(q, k, v, o, s, 1, 1, N, d, c.scale, 0, fa.FA_F32,
                                                                   stream)),
                 "broken": lambda: fa.check(fa.fa_forward_norescale(q, k, v, o, lse, 1, 1, N, d, c.scale, 0, fa.FA_F32,
                                                                    stream)),
+                "split": lambda: fa.check(fa.fa_forward_splitkv(q, k, v, o, lse, ws, 1, 1, N, d, c.scale, 0, nsplit,
+                                                                fa.FA_F32, 0, stream)),
             }
-            row = {"N": N, "d": d}
+            row = {"N": N, "d": d, "nsplit": nsplit}
             for kind, fn in runs.items():
                 if args.counters:
                     fn()
@@ -239,6 +244,7 @@ def lab(args) -> int:
                 row[kind + "_ms"] = round(sorted(ts)[len(ts) // 2], 5)
             if not args.counters:
                 row["unfused_over_fused"] = round(row["unfused_ms"] / row["fused_ms"], 3)
+                row["unfused_over_split"] = round(row["unfused_ms"] / row["split_ms"], 3)
                 row["score_bytes_saved"] = 16 * N * N
             rows.append(row)
     print(json.dumps({"lab": "fused vs unfused attention forward, one head, no mask, float32", "reps": 9,

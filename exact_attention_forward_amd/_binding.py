@@ -35,6 +35,7 @@ SIGNATURES = {
     "fa_backward_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_backward_dkv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_backward_dq_delta": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_forward_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
     "fa_forward_unfused": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_forward_norescale": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_is_supported": (_I, [_I, _I]),
@@ -95,6 +96,11 @@ def check(status: int) -> None:
 def fa_forward(q, k, v, o, lse, B, H, T, hd, scale, causal, dtype, prec, stream) -> int:
     return lib().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, T, hd, scale, int(causal), dtype,
                             prec, _stream(stream))
+
+
+def fa_forward_splitkv(q, k, v, o, lse, ws, B, H, T, hd, scale, causal, nsplit, dtype, prec, stream) -> int:
+    return lib().fa_forward_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), B, H, T, hd, scale,
+                                    int(causal), nsplit, dtype, prec, _stream(stream))
 
 
 def fa_forward_unfused(q, k, v, o, scores, B, H, T, hd, scale, causal, dtype, stream) -> int:

@@ -107,6 +107,24 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
   return run(fa::kFwd, hd, dtype, prec, causal != 0, &a, stream);
 }
 
+int fa_forward_splitkv(const void* q, const void* k, const void* v, float* o, float* lse, float* ws, int B, int H,
+                       int T, int hd, float scale, int causal, int nsplit, fa_dtype dtype, fa_precision prec,
+                       void* stream) {
+  int st = check_common(B, H, T, hd, dtype, prec);
+  if (st) return st;
+  if ((st = check_scale(scale, causal))) return st;
+  if (nsplit < 1 || nsplit > 64) return FA_ERR_ARG;
+  if ((double)B * H > 65535.0) return FA_ERR_ARG;
+  const void* ptrs[] = {q, k, v, o, lse, ws};
+  if ((st = check_ptrs(ptrs, 6))) return st;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_BF16 ? 2 : 4, nr = (size_t)B * H * T;
+  const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}};
+  const Buf out[] = {{o, n * 4}, {lse, nr * 4}, {ws, (size_t)nsplit * (n + nr) * 4}};
+  if ((st = check_alias(in, 3, out, 3))) return st;
+  fa::SplitArgs a{{q, k, v, ws, ws + (size_t)nsplit * n, B, H, T, log2e_scaled(scale)}, o, lse, nsplit};
+  return run(fa::kFwdSplit, hd, dtype, prec, causal != 0, &a, stream);
+}
+
 int fa_forward_norescale(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T,
                          int hd, float scale, int causal, fa_dtype dtype, void* stream) {
   int st = check_common(B, H, T, hd, dtype, FA_PREC_DEFAULT);

@@ -35,6 +35,11 @@ struct FwdArgs {
   int B, H, T;
   float c2;                    // scale * log2(e)
   unsigned one2 = 0x3F803F80u;  // bfloat16 pair (1, 1): a scalar operand for row sums by dot products
+  // Key split (fwd_kernel only): blockIdx.y = s handles keys [s kchunk,
+  // (s + 1) kchunk) and writes its partial O and L at o + s o_split,
+  // lse + s lse_split.  kchunk = 0: one split covering every key.
+  int kchunk = 0;
+  size_t o_split = 0, lse_split = 0;
 };
 
 // PREC: 0 = operands rounded to bfloat16 (or exact f32), 1 = P split into a
@@ -111,18 +116,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   }
 
   const int last_row = min(i0 + BR, T) - 1;
-  const int nkb = CAUSAL ? (last_row / BC + 1) : (T + BC - 1) / BC;
+  // key blocks [kb0, nkb) of this split (all blocks when a.kchunk == 0)
+  const int nkb_all = CAUSAL ? (last_row / BC + 1) : (T + BC - 1) / BC;
+  const int kb0 = a.kchunk ? (int)blockIdx.y * (a.kchunk / BC) : 0;
+  const int nkb = a.kchunk ? min(nkb_all, kb0 + a.kchunk / BC) : nkb_all;
 
   TileCopy<TIn, HD, BC, NT> ck, cv;
-  ck.load(K, rs, 0, T, tid);
-  cv.load(V, rs, 0, T, tid);
+  ck.load(K, rs, kb0 * BC, T, tid);
+  cv.load(V, rs, kb0 * BC, T, tid);
   ck.store(sK[0], LD, tid);
   cv.store(sV[0], LD, tid);
   __syncthreads();
 
-  for (int kb = 0; kb < nkb; ++kb) {
+  for (int kb = kb0; kb < nkb; ++kb) {
     const int j0 = kb * BC;
-    const int buf = kb & 1;
+    const int buf = (kb - kb0) & 1;
     if (kb + 1 < nkb) {
       ck.load(K, rs, j0 + BC, T, tid);
       cv.load(V, rs, j0 + BC, T, tid);
@@ -215,7 +223,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  float* O = a.o + base;
+  float* O = a.o + blockIdx.y * a.o_split + base;
+  float* Lout = a.lse + blockIdx.y * a.lse_split;
 #pragma unroll
   for (int mr = 0; mr < MR; ++mr) {
     const float l = group_sum(lrow[mr]);
@@ -227,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         const int d = 16 * dt + 4 * lg;
         if (d < HD) *reinterpret_cast<f32x4*>(O + (size_t)i * rs + d) = oacc[dt][mr] * inv;
       }
-      if (lg == 0) a.lse[(size_t)bh * T + i] = l > 0.f ? (mrow[mr] + log2f(l)) * kLn2 : -INFINITY;
+      if (lg == 0) Lout[(size_t)bh * T + i] = l > 0.f ? (mrow[mr] + log2f(l)) * kLn2 : -INFINITY;
     }
   }
 }

@@ -5,6 +5,7 @@
 #include "fa_bwd32.hpp"
 #include "fa_fwd.hpp"
 #include "fa_fwd32.hpp"
+#include "fa_split.hpp"
 #include "fa_unfused.hpp"
 
 namespace fa {
@@ -158,13 +159,44 @@ int run_dkv(const BwdArgs& a, hipStream_t s) {
   return launch_status();
 }
 
-enum Stage { kFwd = 0, kDq = 1, kDkv = 2, kDqDelta = 3, kFwdNoRescale = 4 };
+// Split-key forward: partial results of nsplit key ranges into a workspace,
+// then their merge into o and lse.
+struct SplitArgs {
+  FwdArgs f;  // f.o, f.lse point into the workspace
+  float* o;
+  float* lse;
+  int nsplit;
+};
+
+template <typename TIn, int HD, bool CAUSAL, int PREC>
+int run_fwd_split(const SplitArgs& sa, hipStream_t s) {
+  using C = TileCfg<TIn, HD>;
+  constexpr int BR = C::FWD_NW * 16 * C::FWD_MR;
+  FwdArgs a = sa.f;
+  const size_t n = (size_t)a.B * a.T * a.H * HD, nr = (size_t)a.B * a.H * a.T;
+  const int per = (a.T + sa.nsplit - 1) / sa.nsplit;
+  a.kchunk = (per + C::FWD_BC - 1) / C::FWD_BC * C::FWD_BC;
+  a.o_split = n;
+  a.lse_split = nr;
+  const long nqt = (a.T + BR - 1) / BR;
+  hipLaunchKernelGGL((fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC>),
+                     dim3((unsigned)(nqt * a.B * a.H), (unsigned)sa.nsplit), dim3(C::FWD_NW * 64), 0, s, a);
+  if (launch_status()) return -5;
+  MergeArgs m{a.o, a.lse, sa.o, sa.lse, a.B, a.H, a.T, sa.nsplit, n, nr};
+  constexpr int RPB = 256 / (HD / 4);
+  hipLaunchKernelGGL(merge_kernel<HD>, dim3((unsigned)((a.T + RPB - 1) / RPB), (unsigned)(a.B * a.H)), dim3(256), 0,
+                     s, m);
+  return launch_status();
+}
+
+enum Stage { kFwd = 0, kDq = 1, kDkv = 2, kDqDelta = 3, kFwdNoRescale = 4, kFwdSplit = 5 };
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_stage(int stage, const void* args, hipStream_t s) {
   switch (stage) {
     case kFwd: return run_fwd<TIn, HD, CAUSAL, PREC>(*static_cast<const FwdArgs*>(args), s);
     case kFwdNoRescale: return run_fwd<TIn, HD, CAUSAL, PREC, true>(*static_cast<const FwdArgs*>(args), s);
+    case kFwdSplit: return run_fwd_split<TIn, HD, CAUSAL, PREC>(*static_cast<const SplitArgs*>(args), s);
     case kDq: return run_dq<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);
     case kDqDelta: return run_dq<TIn, HD, CAUSAL, PREC, true>(*static_cast<const BwdArgs*>(args), s);
     default: return run_dkv<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);

@@ -242,8 +242,9 @@ def lab_bytes(fetch_db: str, write_db: str) -> dict:
     """(N, d, kind) -> (read bytes, write bytes) from a ``bench.py --lab --counters`` run.
 
     That run launches, for d in (16, 64) and N in (256, ..., 4096): the fused
-    forward (one kernel), the unfused forward (scores, softmax, P V) and the
-    no-rescale control (one kernel), in this order.
+    forward (one kernel), the unfused forward (scores, softmax, P V), the
+    no-rescale control (one kernel) and the split-key forward (partials,
+    merge), in this order.
     """
     f, w = dispatch_counter(fetch_db, "FETCH_SIZE"), dispatch_counter(write_db, "WRITE_SIZE")
     rscale = (1 << 30) / 1024 / max(v for k, v in f if COPY_KERNEL in k)
@@ -253,7 +254,7 @@ def lab_bytes(fetch_db: str, write_db: str) -> dict:
     out, i = {}, 0
     for d in LAB_WIDTHS:
         for N in LAB_SIZES:
-            for kind, nk in (("fused", 1), ("unfused", 3), ("broken", 1)):
+            for kind, nk in (("fused", 1), ("unfused", 3), ("broken", 1), ("split", 2)):
                 r = sum(v for _, v in fk[i:i + nk]) * 1024 * rscale
                 wr = sum(v for _, v in wk[i:i + nk]) * 1024 * wscale
                 out[(N, d, kind)] = (r, wr)
@@ -281,19 +282,23 @@ def lab_report(lab_log: str, fetch_db: str, write_db: str, out_md: str) -> None:
              "float64 reference with the lesson's error bound by tests/test_gpu_lab.py (fused and unfused pass, the "
              "no-rescale control fails).  The lesson predicts that the fused kernel saves exactly 16 N^2 bytes: the "
              "score matrix written, read, written as P and read again.", "",
-             "| N | d | fused ms | unfused ms | no-rescale ms | unfused / fused | fused MB | unfused MB | "
-             "saved MB | predicted 16 N^2 MB | saved / predicted |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+             "| N | d | fused ms | unfused ms | no-rescale ms | split-key ms (splits) | unfused / fused | "
+             "unfused / split | fused MB | unfused MB | saved MB | predicted 16 N^2 MB | saved / predicted |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in (rec or {}).get("rows", []):
         N, d = r["N"], r["d"]
         fb = sum(by[(N, d, "fused")])
         ub = sum(by[(N, d, "unfused")])
         pred = 16 * N * N
         lines.append(f"| {N} | {d} | {r['fused_ms']:.4f} | {r['unfused_ms']:.4f} | {r['broken_ms']:.4f} | "
-                     f"{r['unfused_over_fused']:.2f} | {fb / 1e6:.2f} | {ub / 1e6:.2f} | {(ub - fb) / 1e6:.2f} | "
+                     f"{r['split_ms']:.4f} ({r['nsplit']}) | {r['unfused_over_fused']:.2f} | "
+                     f"{r['unfused_over_split']:.2f} | {fb / 1e6:.2f} | {ub / 1e6:.2f} | {(ub - fb) / 1e6:.2f} | "
                      f"{pred / 1e6:.2f} | {(ub - fb) / pred:.2f} |")
     lines += ["", "One head gives the fused kernel only ceil(N / 128) workgroups (32 at N = 4096) on 256 compute "
               "units, while the unfused kernels spread N^2 / 4096 score tiles over the chip; the time is set by that "
-              "parallelism (and, at d = 16, by the score traffic), not by global memory alone."]
+              "parallelism (and, at d = 16, by the score traffic), not by global memory alone.  The split-key "
+              "forward (fa_forward_splitkv) keeps the fused kernel's traffic but runs (N / 128)^2 workgroups and "
+              "merges their partial (O, L) states."]
     Path(out_md).write_text("\n".join(lines) + "\n")
 
 

@@ -75,6 +75,26 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
                float scale, int causal, fa_dtype dtype, fa_precision prec, void* stream);
 
 /*
+ * Split-key forward: the same outputs as fa_forward (o, lse), computed by
+ * splitting each row's keys into nsplit contiguous ranges processed by
+ * separate workgroups, each writing a partial (o_s, lse_s) to `ws`, followed
+ * by a merge kernel that combines the partials with the associative merge of
+ * the online normaliser (forward notes, the merge identity after the loop;
+ * the fused-attention lesson, block "sources.onlineSoftmax", claim that the
+ * merge is associative and commutative).  More workgroups per query tile:
+ * for few (batch, head) pairs and long T.  Results equal fa_forward's up to
+ * float32 rounding order (not bit for bit).
+ *   ws      float32 workspace of nsplit * (B*T*H*hd + B*H*T) elements,
+ *           caller-allocated; overwritten
+ *   nsplit  1 .. 64
+ * Other arguments and the contract as fa_forward.  Extra limit: B*H <=
+ * 65535.
+ */
+int fa_forward_splitkv(const void* q, const void* k, const void* v, float* o, float* lse, float* ws, int B, int H,
+                       int T, int hd, float scale, int causal, int nsplit, fa_dtype dtype, fa_precision prec,
+                       void* stream);
+
+/*
  * Unfused forward (float32 inputs only), the comparator of the fused-attention
  * lesson ("Lesson K23, fused attention", blocks "sources" -- Algorithm 0 of
  * the FlashAttention paper -- and "lab"): three kernels in order on `stream`,

@@ -154,3 +154,18 @@ def test_unfused_and_control_entry_points_validate(lib):
         fa.FA_ERR_ARG
     assert fa.fa_forward_norescale(P[0], P[1], P[2], P[0], P[4], 1, 2, 8, 64, 0.1, 0, fa.FA_F32, None) == \
         fa.FA_ERR_ALIAS
+
+
+def test_splitkv_validates(lib):
+    args = lambda **kw: {**dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], ws=P[5], B=1, H=2, T=8, hd=64, scale=0.1,
+                                causal=1, nsplit=4, dtype=fa.FA_F32, prec=0, stream=None), **kw}
+    call = lambda **kw: fa.fa_forward_splitkv(*args(**kw).values())
+    assert call(nsplit=0) == fa.FA_ERR_ARG
+    assert call(nsplit=65) == fa.FA_ERR_ARG
+    assert call(ws=None) == fa.FA_ERR_ARG
+    assert call(ws=P[5] + 8) == fa.FA_ERR_ALIGN
+    assert call(ws=P[0]) == fa.FA_ERR_ALIAS
+    assert call(ws=P[3] + 1024) == fa.FA_ERR_ALIAS
+    assert call(H=1 << 16) == fa.FA_ERR_ARG
+    assert call(hd=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(dtype=fa.FA_BF16, hd=32) == fa.FA_ERR_UNSUPPORTED
