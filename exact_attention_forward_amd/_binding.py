@@ -13,6 +13,7 @@ from pathlib import Path
 
 FA_F32 = 0
 FA_BF16 = 1
+FA_F16 = 2
 FA_PREC_DEFAULT = 0
 FA_PREC_BF16 = 1
 FA_PREC_BF16X2 = 2
@@ -38,6 +39,7 @@ SIGNATURES = {
     "fa_forward_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
     "fa_forward_unfused": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_forward_norescale": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_forward_nomax": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_is_supported": (_I, [_I, _I]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -111,6 +113,11 @@ def fa_forward_unfused(q, k, v, o, scores, B, H, T, hd, scale, causal, dtype, st
 def fa_forward_norescale(q, k, v, o, lse, B, H, T, hd, scale, causal, dtype, stream) -> int:
     return lib().fa_forward_norescale(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, T, hd, scale, int(causal),
                                       dtype, _stream(stream))
+
+
+def fa_forward_nomax(q, k, v, o, lse, B, H, T, hd, scale, causal, dtype, stream) -> int:
+    return lib().fa_forward_nomax(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, T, hd, scale, int(causal), dtype,
+                                  _stream(stream))
 
 
 def fa_backward(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, T, hd, scale, causal, dtype, prec, stream) -> int:

@@ -16,7 +16,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 OBJ = PKG / "_build"
 LIB = PKG / "libfa.so"
-SOURCES = ["fa_api.hip", "fa_inst_f32.hip", "fa_inst_bf16.hip"]
+SOURCES = ["fa_api.hip", "fa_inst_f32.hip", "fa_inst_bf16.hip", "fa_inst_f16.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed f32 VALU ops.

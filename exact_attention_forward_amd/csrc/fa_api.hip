@@ -41,20 +41,20 @@ int check_ptrs(const void* const* ps, int n) {
 
 int supported(int hd, int dtype) {
   if (dtype == FA_F32) return hd == 8 || hd == 16 || hd == 32 || hd == 64 || hd == 128;
-  if (dtype == FA_BF16) return hd == 64 || hd == 128;
+  if (dtype == FA_BF16 || dtype == FA_F16) return hd == 64 || hd == 128;
   return 0;
 }
 
 // Shape, dtype and precision checks shared by every entry point.
 int check_common(int B, int H, int T, int hd, int dtype, int prec) {
   if (B < 1 || H < 1 || T < 1 || hd < 1) return FA_ERR_ARG;
-  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_ARG;
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_ARG;
   if (prec != FA_PREC_DEFAULT && prec != FA_PREC_BF16 && prec != FA_PREC_BF16X2) return FA_ERR_ARG;
   const double elems = (double)B * H * T * hd;
   if (elems >= 1099511627776.0) return FA_ERR_ARG;  // 2^40
   if ((double)B * H * T >= 2147483647.0) return FA_ERR_ARG;
   if (!supported(hd, dtype)) return FA_ERR_UNSUPPORTED;
-  if (dtype == FA_F32 && prec != FA_PREC_DEFAULT) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && prec != FA_PREC_DEFAULT) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -68,8 +68,9 @@ int prec_index(int prec) { return prec == FA_PREC_BF16X2 ? 1 : 0; }
 
 int run(int stage, int hd, int dtype, int prec, bool causal, const void* args, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == FA_F32 ? fa::stage_f32(stage, hd, args, causal, s)
-                         : fa::stage_bf16(stage, hd, args, causal, prec_index(prec), s);
+  if (dtype == FA_F32) return fa::stage_f32(stage, hd, args, causal, s);
+  if (dtype == FA_F16) return fa::stage_f16(stage, hd, args, causal, 0, s);
+  return fa::stage_bf16(stage, hd, args, causal, prec_index(prec), s);
 }
 
 float log2e_scaled(float scale) { return (float)((double)scale * 1.4426950408889634); }
@@ -99,7 +100,7 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
   if ((st = check_scale(scale, causal))) return st;
   const void* ptrs[] = {q, k, v, o, lse};
   if ((st = check_ptrs(ptrs, 5))) return st;
-  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_BF16 ? 2 : 4;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2;
   const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}};
   const Buf out[] = {{o, n * 4}, {lse, (size_t)B * H * T * 4}};
   if ((st = check_alias(in, 3, out, 2))) return st;
@@ -117,7 +118,7 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, float* o, fl
   if ((double)B * H > 65535.0) return FA_ERR_ARG;
   const void* ptrs[] = {q, k, v, o, lse, ws};
   if ((st = check_ptrs(ptrs, 6))) return st;
-  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_BF16 ? 2 : 4, nr = (size_t)B * H * T;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2, nr = (size_t)B * H * T;
   const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}};
   const Buf out[] = {{o, n * 4}, {lse, nr * 4}, {ws, (size_t)nsplit * (n + nr) * 4}};
   if ((st = check_alias(in, 3, out, 3))) return st;
@@ -125,20 +126,30 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, float* o, fl
   return run(fa::kFwdSplit, hd, dtype, prec, causal != 0, &a, stream);
 }
 
-int fa_forward_norescale(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T,
-                         int hd, float scale, int causal, fa_dtype dtype, void* stream) {
+static int control_forward(int stage, const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                           int H, int T, int hd, float scale, int causal, fa_dtype dtype, void* stream) {
   int st = check_common(B, H, T, hd, dtype, FA_PREC_DEFAULT);
   if (st) return st;
-  if (dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_BF16) return FA_ERR_UNSUPPORTED;
   if ((st = check_scale(scale, causal))) return st;
   const void* ptrs[] = {q, k, v, o, lse};
   if ((st = check_ptrs(ptrs, 5))) return st;
-  const size_t n = (size_t)B * T * H * hd;
-  const Buf in[] = {{q, n * 4}, {k, n * 4}, {v, n * 4}};
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2;
+  const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}};
   const Buf out[] = {{o, n * 4}, {lse, (size_t)B * H * T * 4}};
   if ((st = check_alias(in, 3, out, 2))) return st;
   fa::FwdArgs a{q, k, v, o, lse, B, H, T, log2e_scaled(scale)};
-  return run(fa::kFwdNoRescale, hd, dtype, FA_PREC_DEFAULT, causal != 0, &a, stream);
+  return run(stage, hd, dtype, FA_PREC_DEFAULT, causal != 0, &a, stream);
+}
+
+int fa_forward_norescale(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T,
+                         int hd, float scale, int causal, fa_dtype dtype, void* stream) {
+  return control_forward(fa::kFwdNoRescale, q, k, v, o, lse, B, H, T, hd, scale, causal, dtype, stream);
+}
+
+int fa_forward_nomax(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T, int hd,
+                     float scale, int causal, fa_dtype dtype, void* stream) {
+  return control_forward(fa::kFwdNoMax, q, k, v, o, lse, B, H, T, hd, scale, causal, dtype, stream);
 }
 
 int fa_forward_unfused(const void* q, const void* k, const void* v, float* o, float* scores, int B, int H, int T,
@@ -165,7 +176,7 @@ int fa_backward_delta(const float* o, const void* dO, float* delta, int B, int H
   if (st) return st;
   const void* ptrs[] = {o, dO, delta};
   if ((st = check_ptrs(ptrs, 3))) return st;
-  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_BF16 ? 2 : 4;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2;
   const Buf in[] = {{o, n * 4}, {dO, n * es}};
   const Buf out[] = {{delta, (size_t)B * H * T * 4}};
   if ((st = check_alias(in, 2, out, 1))) return st;
@@ -175,7 +186,8 @@ int fa_backward_delta(const float* o, const void* dO, float* delta, int B, int H
   a.delta = delta;
   a.B = B, a.H = H, a.T = T;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == FA_F32 ? fa::delta_f32(hd, a, s) : fa::delta_bf16(hd, a, s);
+  if (dtype == FA_F32) return fa::delta_f32(hd, a, s);
+  return dtype == FA_F16 ? fa::delta_f16(hd, a, s) : fa::delta_bf16(hd, a, s);
 }
 
 static int check_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO,
@@ -186,7 +198,7 @@ static int check_dq(const void* q, const void* k, const void* v, const float* ls
   if ((st = check_scale(scale, causal))) return st;
   const void* ptrs[] = {q, k, v, lse, dO, delta, dq};
   if ((st = check_ptrs(ptrs, 7))) return st;
-  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_BF16 ? 2 : 4, nr = (size_t)B * H * T * 4;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2, nr = (size_t)B * H * T * 4;
   const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}, {lse, nr}, {dO, n * es}, {delta, nr}};
   const Buf out[] = {{dq, n * 4}};
   return check_alias(in, 6, out, 1);
@@ -200,7 +212,7 @@ static int check_dkv(const void* q, const void* k, const void* v, const float* l
   if ((st = check_scale(scale, causal))) return st;
   const void* ptrs[] = {q, k, v, lse, dO, delta, dk, dv};
   if ((st = check_ptrs(ptrs, 8))) return st;
-  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_BF16 ? 2 : 4, nr = (size_t)B * H * T * 4;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2, nr = (size_t)B * H * T * 4;
   const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}, {lse, nr}, {dO, n * es}, {delta, nr}};
   const Buf out[] = {{dk, n * 4}, {dv, n * 4}};
   return check_alias(in, 6, out, 2);
@@ -239,7 +251,7 @@ int fa_backward_dq_delta(const void* q, const void* k, const void* v, const floa
   if ((st = check_scale(scale, causal))) return st;
   const void* ptrs[] = {q, k, v, o, lse, dO, dq, delta};
   if ((st = check_ptrs(ptrs, 8))) return st;
-  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_BF16 ? 2 : 4, nr = (size_t)B * H * T * 4;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2, nr = (size_t)B * H * T * 4;
   const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}, {o, n * 4}, {lse, nr}, {dO, n * es}};
   const Buf out[] = {{dq, n * 4}, {delta, nr}};
   if ((st = check_alias(in, 6, out, 2))) return st;
@@ -255,7 +267,7 @@ int fa_backward(const void* q, const void* k, const void* v, const float* o, con
   if ((st = check_scale(scale, causal))) return st;
   const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv, delta};
   if ((st = check_ptrs(ptrs, 10))) return st;
-  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_BF16 ? 2 : 4, nr = (size_t)B * H * T * 4;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2, nr = (size_t)B * H * T * 4;
   const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}, {o, n * 4}, {lse, nr}, {dO, n * es}};
   const Buf out[] = {{dq, n * 4}, {dk, n * 4}, {dv, n * 4}, {delta, nr}};
   if ((st = check_alias(in, 6, out, 4))) return st;

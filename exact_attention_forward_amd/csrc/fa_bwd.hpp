@@ -17,6 +17,7 @@
 //  * dK/dV kernel: lanes own key rows.  S = Q K^T and dP = dO V^T give each
 //    lane one key column; P and dS feed dV^T += dO^T P and dK^T += Q^T dS.
 #pragma once
+#include <type_traits>
 #include "fa_common.hpp"
 
 namespace fa {
@@ -53,6 +54,10 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
     if (sizeof(TIn) == 4) {
       const float4 g = *reinterpret_cast<const float4*>(static_cast<const float*>(a.dO) + row * HD + 4 * sub);
       d0 = g.x, d1 = g.y, d2 = g.z, d3 = g.w;
+    } else if (std::is_same<TIn, f16_t>::value) {
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      const h4 g = *reinterpret_cast<const h4*>(static_cast<const uint16_t*>(a.dO) + row * HD + 4 * sub);
+      d0 = (float)g[0], d1 = (float)g[1], d2 = (float)g[2], d3 = (float)g[3];
     } else {
       const uint2 g = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.dO) + row * HD + 4 * sub);
       d0 = __uint_as_float(g.x << 16);

@@ -29,6 +29,11 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 struct bf16_t {
   uint16_t bits;
 };
+// IEEE binary16 storage (the kernels convert through _Float16).
+struct f16_t {
+  uint16_t bits;
+};
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -176,6 +181,60 @@ struct Mma<bf16_t> {
     frag z;
 #pragma unroll
     for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
+    return z;
+  }
+};
+
+// IEEE half inputs: v_mfma_f32_16x16x32_f16, the same lane layouts as the
+// bfloat16 policy (16-bit elements, eight per operand).
+__device__ __forceinline__ f16x8 cvt8h(const f32x4& a, const f32x4& b) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (_Float16)a[e];
+    r[4 + e] = (_Float16)b[e];
+  }
+  return r;
+}
+
+template <>
+struct Mma<f16_t> {
+  static constexpr int KS = 32;
+  static constexpr int CH = 32;
+  static constexpr int NSTEP = 1;
+  static constexpr int VEC = 8;
+  using frag = f16x8;
+
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag ld_row(const f16_t* X, int ld, int row0, int k0, int li, int lg) {
+    return *reinterpret_cast<const frag*>(X + (row0 + li) * ld + k0 + 8 * lg);
+  }
+  // Transposing reads as in Mma<bf16_t>::ld_trans (16-bit elements).
+  __device__ __forceinline__ static frag ld_trans(const f16_t* Y, int ld, int k0, int m0, int step, int li, int lg) {
+    const f16_t* p = Y + (k0 + 4 * lg + (li >> 2)) * ld + m0 + 4 * (li & 3);
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * ld));
+    typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+    i16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(frag, r);
+  }
+  __device__ __forceinline__ static frag pack(const f32x4* c, int step) { return cvt8h(c[0], c[1]); }
+  __device__ __forceinline__ static frag pack_lo(const f32x4* c, int step) {
+    f32x4 a, b;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a[r] = c[0][r] - (float)(_Float16)c[0][r];
+      b[r] = c[1][r] - (float)(_Float16)c[1][r];
+    }
+    return cvt8h(a, b);
+  }
+  __device__ __forceinline__ static frag ld_row_global(const f16_t* X, size_t ld, int row, int nrows, int k0, int lg) {
+    if (row < nrows) return *reinterpret_cast<const frag*>(X + (size_t)row * ld + k0 + 8 * lg);
+    frag z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (_Float16)0.f;
     return z;
   }
 };

@@ -44,12 +44,17 @@ struct FwdArgs {
 
 // PREC: 0 = operands rounded to bfloat16 (or exact f32), 1 = P split into a
 // bfloat16 high part and a bfloat16 residual (two products).
-// NORESCALE: the control variant of the fused-attention lesson (blocks
-// "controls" and "correctness"): when a row's running max rises, the running
-// sum l and the accumulated output are NOT multiplied by alpha.  The result is
-// wrong whenever a later key block raises a row's max; it exists only so that
-// the error checker can be shown to catch it.
-template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int MR, int BC, bool NORESCALE = false>
+// CONTROL (deliberately wrong variants that exist only so that checks can be
+// shown to reject them):
+//   kCtlNoRescale  the "broken" kernel of the fused-attention lesson (blocks
+//                  "controls" and "correctness"): when a row's running max
+//                  rises, l and the accumulated output are NOT multiplied by
+//                  alpha; wrong whenever a later key block raises a row's max;
+//   kCtlNoMax      the unsafe softmax: no max is subtracted, p = exp(s); with
+//                  half-precision P operands any score >= ln 65520 overflows
+//                  (lesson, block "overflow").
+enum Control { kCtlNone = 0, kCtlNoRescale = 1, kCtlNoMax = 2 };
+template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int MR, int BC, int CONTROL = kCtlNone>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   using M = Mma<TIn>;
   using frag = typename M::frag;
@@ -177,8 +182,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
           for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[mr][jt][r]);
         mx = group_max(mx);
         const float mold = mrow[mr];
-        const float mnew = fmaxf(mold, mx * c2);
-        const float alpha = NORESCALE ? 1.f : ((mold == -INFINITY) ? 0.f : fast_exp2(mold - mnew));
+        const float mnew = CONTROL == kCtlNoMax ? 0.f : fmaxf(mold, mx * c2);
+        const float alpha = CONTROL != kCtlNone ? 1.f : ((mold == -INFINITY) ? 0.f : fast_exp2(mold - mnew));
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
         mrow[mr] = mnew;
         float ls = 0.f;

@@ -1,6 +1,8 @@
 // Kernel instantiation and launch helpers shared by the per-dtype translation
 // units.  Tile shapes per (input type, head dim) live in TileCfg.
 #pragma once
+#include <type_traits>
+
 #include "fa_bwd.hpp"
 #include "fa_bwd32.hpp"
 #include "fa_fwd.hpp"
@@ -56,6 +58,8 @@ struct TileCfg<bf16_t, 64> {
   static constexpr int DQ_NW = 4, DQ_MR = 2, DQ_BC = 64;
   static constexpr int DKV_NW = 4, DKV_MR = 2, DKV_BQ = 64;
 };
+template <int HD>
+struct TileCfg<f16_t, HD> : TileCfg<bf16_t, HD> {};
 template <>
 struct TileCfg<bf16_t, 128> {
   static constexpr int FWD_NW = 4, FWD_MR = 2, FWD_BC = 64;
@@ -91,11 +95,14 @@ inline long persistent_grid(K kernel, int threads, long items) {
   return items < slots ? items : slots;
 }
 
-template <typename TIn, int HD, bool CAUSAL, int PREC, bool NORESCALE = false>
+template <typename TIn>
+constexpr bool is_bf16 = std::is_same<TIn, bf16_t>::value;
+
+template <typename TIn, int HD, bool CAUSAL, int PREC, int CONTROL = kCtlNone>
 int run_fwd(const FwdArgs& a, hipStream_t s) {
-  if constexpr (NORESCALE && sizeof(TIn) == 2) {
-    return -3;  // the control variant is built for float32 inputs only
-  } else if constexpr (sizeof(TIn) == 2) {
+  if constexpr (CONTROL != kCtlNone && is_bf16<TIn>) {
+    return -3;  // the control variants are built for float32 and half inputs only
+  } else if constexpr (is_bf16<TIn>) {
     using C = TileCfg32<HD>;
     auto* k = &fwd32_kernel<HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC, C::FWD_MS>;
     constexpr int BR = C::FWD_NW * 32 * C::FWD_MS;
@@ -107,7 +114,7 @@ int run_fwd(const FwdArgs& a, hipStream_t s) {
     constexpr int BR = C::FWD_NW * 16 * C::FWD_MR;
     const long nqt = (a.T + BR - 1) / BR;
     const long grid = nqt * a.B * a.H;
-    hipLaunchKernelGGL((fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC, NORESCALE>),
+    hipLaunchKernelGGL((fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC, CONTROL>),
                        dim3((unsigned)grid), dim3(C::FWD_NW * 64), 0, s, a);
     return launch_status();
   }
@@ -123,14 +130,14 @@ int run_delta(const BwdArgs& a, hipStream_t s) {
 
 template <typename TIn, int HD, bool CAUSAL, int PREC, bool FUSE_D = false>
 int run_dq(const BwdArgs& a, hipStream_t s) {
-  if constexpr (sizeof(TIn) == 2) {
+  if constexpr (is_bf16<TIn>) {
     using C = TileCfg32<HD>;
     auto* k = &dq32_kernel<HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC, FUSE_D>;
     const long items = (long)((a.T + C::DQ_NW * 32 - 1) / (C::DQ_NW * 32)) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DQ_NW * 64, items)), dim3(C::DQ_NW * 64), 0, s, a);
     return launch_status();
   }
-  if constexpr (FUSE_D) {  // float32 path: the pre-pass, then the dQ kernel
+  if constexpr (FUSE_D) {  // float32 / half path: the pre-pass, then the dQ kernel
     const int st = run_delta<TIn, HD>(a, s);
     if (st) return st;
   }
@@ -144,7 +151,7 @@ int run_dq(const BwdArgs& a, hipStream_t s) {
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_dkv(const BwdArgs& a, hipStream_t s) {
-  if constexpr (sizeof(TIn) == 2) {
+  if constexpr (is_bf16<TIn>) {
     using C = TileCfg32<HD>;
     auto* k = &dkv32_kernel<HD, CAUSAL, PREC, C::DKV_NW, C::DKV_BQ>;
     const long items = (long)((a.T + C::DKV_NW * 32 - 1) / (C::DKV_NW * 32)) * a.B * a.H;
@@ -189,13 +196,14 @@ int run_fwd_split(const SplitArgs& sa, hipStream_t s) {
   return launch_status();
 }
 
-enum Stage { kFwd = 0, kDq = 1, kDkv = 2, kDqDelta = 3, kFwdNoRescale = 4, kFwdSplit = 5 };
+enum Stage { kFwd = 0, kDq = 1, kDkv = 2, kDqDelta = 3, kFwdNoRescale = 4, kFwdSplit = 5, kFwdNoMax = 6 };
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_stage(int stage, const void* args, hipStream_t s) {
   switch (stage) {
     case kFwd: return run_fwd<TIn, HD, CAUSAL, PREC>(*static_cast<const FwdArgs*>(args), s);
-    case kFwdNoRescale: return run_fwd<TIn, HD, CAUSAL, PREC, true>(*static_cast<const FwdArgs*>(args), s);
+    case kFwdNoRescale: return run_fwd<TIn, HD, CAUSAL, PREC, kCtlNoRescale>(*static_cast<const FwdArgs*>(args), s);
+    case kFwdNoMax: return run_fwd<TIn, HD, CAUSAL, PREC, kCtlNoMax>(*static_cast<const FwdArgs*>(args), s);
     case kFwdSplit: return run_fwd_split<TIn, HD, CAUSAL, PREC>(*static_cast<const SplitArgs*>(args), s);
     case kDq: return run_dq<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);
     case kDqDelta: return run_dq<TIn, HD, CAUSAL, PREC, true>(*static_cast<const BwdArgs*>(args), s);
@@ -216,6 +224,8 @@ int run_stage_hd(int stage, const void* args, bool causal, int prec, hipStream_t
 // operand, 1 split operand.  Return 0, -3 (head dim not built) or -5.
 int stage_f32(int stage, int hd, const void* args, bool causal, hipStream_t s);
 int stage_bf16(int stage, int hd, const void* args, bool causal, int prec, hipStream_t s);
+int stage_f16(int stage, int hd, const void* args, bool causal, int prec, hipStream_t s);
+int delta_f16(int hd, const BwdArgs& a, hipStream_t s);
 int delta_f32(int hd, const BwdArgs& a, hipStream_t s);
 int unfused_f32(int hd, const UnfusedArgs& a, bool causal, hipStream_t s);
 int delta_bf16(int hd, const BwdArgs& a, hipStream_t s);

@@ -13,7 +13,9 @@ Recipe (the same for every workload):
   multiplied by 8 in float32 (a power of two, so exact);
 * float32 storage: float64 -> float32 round-to-nearest-even;
 * bfloat16 storage: the float32 values rounded to bfloat16 (round to nearest,
-  ties to even), kept as their 16-bit patterns in ``uint16`` arrays.
+  ties to even), kept as their 16-bit patterns in ``uint16`` arrays;
+* half storage: the float32 values rounded to IEEE binary16 (numpy's
+  round-to-nearest-even conversion), kept as their 16-bit patterns.
 
 All tensors are laid out [B, T, H, hd], row-major.
 """
@@ -26,6 +28,7 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -61,20 +64,22 @@ class Case:
 
     def f64(self, name: str) -> np.ndarray:
         """The exact values the device receives, widened to float64."""
-        a = getattr(self, name)
-        if self.dtype == BF16:
-            return bf16_bits_to_f32(a).astype(np.float64)
-        return a.astype(np.float64)
+        return _widen(getattr(self, name), self.dtype)
 
     def head_f64(self, name: str, b: int, h: int) -> np.ndarray:
-        a = getattr(self, name)[b, :, h, :]
-        if self.dtype == BF16:
-            return bf16_bits_to_f32(a).astype(np.float64)
-        return a.astype(np.float64)
+        return _widen(getattr(self, name)[b, :, h, :], self.dtype)
 
     @property
     def itemsize(self) -> int:
-        return 2 if self.dtype == BF16 else 4
+        return 4 if self.dtype == F32 else 2
+
+
+def _widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == BF16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    if dtype == F16:
+        return np.ascontiguousarray(a).view(np.float16).astype(np.float64)
+    return a.astype(np.float64)
 
 
 def make_case(name: str, B: int, H: int, T: int, hd: int, dtype: str, causal: bool, seed: int,
@@ -93,6 +98,8 @@ def make_case(name: str, B: int, H: int, T: int, hd: int, dtype: str, causal: bo
         scale = 1.0 / math.sqrt(hd)
     if dtype == BF16:
         q, k, v, do = (f32_to_bf16_bits(a) for a in (q, k, v, do))
+    elif dtype == F16:
+        q, k, v, do = (a.astype(np.float16).view(np.uint16) for a in (q, k, v, do))
     elif dtype != F32:
         raise ValueError(dtype)
     return Case(name, B, H, T, hd, dtype, causal, float(scale), seed, q, k, v, do)

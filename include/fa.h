@@ -12,8 +12,9 @@
  * Layout.   q, k, v, dO, o, dq, dk, dv are dense row-major [B, T, H, hd]
  *           tensors (the [B, T, C] activations with C = H * hd of the forward
  *           notes).  lse and delta are dense [B, H, T] float32 vectors.
- * Dtypes.   Inputs q, k, v, dO are FA_F32 (float32) or FA_BF16 (bfloat16
- *           bits).  Every output and workspace is float32.
+ * Dtypes.   Inputs q, k, v, dO are FA_F32 (float32), FA_BF16 (bfloat16
+ *           bits) or FA_F16 (IEEE binary16 bits).  Every output and
+ *           workspace is float32.
  * Mask.     causal != 0 keeps key j for query i iff j <= i (diagonal kept);
  *           causal == 0 keeps every key.  Self-attention only (one T).
  * Scale.    Scores are scale * <q_i, k_j>; scale must be finite and > 0
@@ -37,13 +38,14 @@
 extern "C" {
 #endif
 
-typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 } fa_dtype;
 
 /*
  * Operand precision of the two products whose left factor is computed inside
  * the kernel (P in P.V and dV, dS in dQ and dK).  Only meaningful for FA_BF16
  * inputs; FA_F32 inputs accept FA_PREC_DEFAULT only and compute every product
- * in float32.
+ * in float32; FA_F16 inputs accept FA_PREC_DEFAULT only and round P and dS to
+ * binary16 for their products.
  *   FA_PREC_DEFAULT  same as FA_PREC_BF16 for bfloat16 inputs
  *   FA_PREC_BF16     P and dS rounded to bfloat16 before the matrix product
  *   FA_PREC_BF16X2   P and dS split into a bfloat16 value and a bfloat16
@@ -119,12 +121,26 @@ int fa_forward_unfused(const void* q, const void* k, const void* v, float* o, fl
  * "broken" kernel of the fused-attention lesson, blocks "controls" and
  * "correctness"; the rescale is step 3 of "Loop (per (b, h, Q-tile))" in the
  * forward notes).  It agrees with fa_forward only while every row's max is
- * set by its first key block (T <= 32 keys here), and exists so that error
- * checkers can be shown to reject it.  Same arguments and contract as
- * fa_forward (precision FA_PREC_DEFAULT); FA_ERR_UNSUPPORTED for bfloat16.
+ * set by its first key block (T <= 32 keys for float32, 64 for half here),
+ * and exists so that error checkers can be shown to reject it.  Same
+ * arguments and contract as fa_forward (precision FA_PREC_DEFAULT); float32
+ * and half inputs; FA_ERR_UNSUPPORTED for bfloat16.
  */
 int fa_forward_norescale(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T,
                          int hd, float scale, int causal, fa_dtype dtype, void* stream);
+
+/*
+ * Control variant of fa_forward, deliberately UNSAFE: the softmax without the
+ * max subtracted, p = exp(s) (the naive softmax of the fused-attention
+ * lesson, block "overflow"; the max subtraction is step 3 of "Loop (per (b,
+ * h, Q-tile))" in the forward notes).  With FA_F16 inputs the weights enter
+ * the P.V product as binary16, so any visible score s >= ln 65520 = 11.09
+ * becomes an infinite weight and its row of o is not finite; with FA_F32
+ * inputs the same happens only above ln(float max) = 88.7.  lse = ln(sum p).
+ * Same arguments and contract as fa_forward_norescale.
+ */
+int fa_forward_nomax(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T, int hd,
+                     float scale, int causal, fa_dtype dtype, void* stream);
 
 /*
  * Backward pass with recomputation (backward notes, "The math (FA2 backward
@@ -181,7 +197,7 @@ int fa_backward_dkv(const void* q, const void* k, const void* v, const float* ls
                     const float* delta, float* dk, float* dv, int B, int H, int T, int hd, float scale,
                     int causal, fa_dtype dtype, fa_precision prec, void* stream);
 
-/* 1 if (hd, dtype) is built (f32: hd in {8,16,32,64,128}; bf16: {64,128}), else 0. */
+/* 1 if (hd, dtype) is built (f32: hd in {8,16,32,64,128}; bf16 and f16: {64,128}), else 0. */
 int fa_is_supported(int hd, fa_dtype dtype);
 
 /* Static string naming a status code; never NULL. */

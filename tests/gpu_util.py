@@ -16,6 +16,8 @@ def to_device(case: I.Case, name: str) -> torch.Tensor:
     a = getattr(case, name)
     if case.dtype == I.BF16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    if case.dtype == I.F16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.float16)).cuda()
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
@@ -23,7 +25,7 @@ def run_case(case: I.Case, prec: int = fa.FA_PREC_DEFAULT, poison: bool = True, 
     """Forward + backward through the C ABI.  Outputs start as NaN so unwritten elements show."""
     q, k, v, do = (to_device(case, n) for n in ("q", "k", "v", "do"))
     B, T, H, hd = q.shape
-    dtc = fa.FA_BF16 if case.dtype == I.BF16 else fa.FA_F32
+    dtc = {I.BF16: fa.FA_BF16, I.F16: fa.FA_F16}.get(case.dtype, fa.FA_F32)
     fill = float("nan") if poison else 0.0
     mk = lambda *s: torch.full(s, fill, device="cuda", dtype=torch.float32)
     o, lse = mk(B, T, H, hd), mk(B, H, T)

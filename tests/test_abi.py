@@ -47,6 +47,8 @@ def test_support_table_and_status_strings(lib):
         assert fa.fa_is_supported(hd, fa.FA_F32) == 1
     for hd in (64, 128):
         assert fa.fa_is_supported(hd, fa.FA_BF16) == 1
+        assert fa.fa_is_supported(hd, fa.FA_F16) == 1
+    assert fa.fa_is_supported(32, fa.FA_F16) == 0
     for hd, dt in ((4, fa.FA_F32), (96, fa.FA_F32), (32, fa.FA_BF16), (256, fa.FA_BF16), (64, 7)):
         assert fa.fa_is_supported(hd, dt) == 0
     for st in (fa.FA_OK, fa.FA_ERR_ARG, fa.FA_ERR_ALIGN, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_ALIAS, fa.FA_ERR_LAUNCH, 9):
@@ -169,3 +171,16 @@ def test_splitkv_validates(lib):
     assert call(H=1 << 16) == fa.FA_ERR_ARG
     assert call(hd=96) == fa.FA_ERR_UNSUPPORTED
     assert call(dtype=fa.FA_BF16, hd=32) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_half_inputs_validate(lib):
+    assert fwd(dtype=fa.FA_F16, hd=32) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(dtype=fa.FA_F16, prec=fa.FA_PREC_BF16) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(dtype=fa.FA_F16, prec=fa.FA_PREC_BF16X2) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(dtype=3) == fa.FA_ERR_ARG
+    # half inputs are 2 bytes: o may start right after q's 2-byte extent
+    n = 1 * 8 * 2 * 64
+    assert fwd(dtype=fa.FA_F16, o=P[0] + 2 * n - 16) == fa.FA_ERR_ALIAS
+    assert fa.fa_forward_nomax(P[0], P[1], P[2], P[3], P[4], 1, 2, 8, 64, 0.1, 0, fa.FA_BF16, None) == \
+        fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_forward_nomax(P[0], P[1], P[2], P[3], None, 1, 2, 8, 64, 0.1, 0, fa.FA_F16, None) == fa.FA_ERR_ARG
