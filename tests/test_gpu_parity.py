@@ -112,6 +112,22 @@ def test_gpt2m_bf16_sampled(gpt2m_bf16):
     check_sampled(gpt2m_bf16, fa.FA_PREC_BF16, BF16_TOL, SAMPLE_HEADS)
 
 
+# Ragged T with enough (query or key tile, head) items that every persistent
+# workgroup walks several of them: the first block and rows of a workgroup's
+# next item are fetched while it finishes the current one.  Sampled heads come
+# from both ends of the schedule.
+MULTI_ITEM = [(2, 128, 1000, 64), (1, 64, 1000, 128)]
+
+
+@pytest.mark.parametrize("shape", MULTI_ITEM, ids=lambda s: "B{}H{}T{}hd{}".format(*s))
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_ragged_multi_item_sampled(shape, causal):
+    B, H, T, hd = shape
+    c = I.make_case("multi_item", B, H, T, hd, I.BF16, causal, 7 + hd)
+    heads = [(0, 0), (0, 37), (B - 1, H // 2), (B - 1, H - 1)]
+    check_sampled(c, fa.FA_PREC_BF16, BF16_TOL, heads)
+
+
 def test_long_bf16_split_sampled():
     c = I.long_case()
     check_sampled(c, fa.FA_PREC_BF16X2, BF16_TOL, [(0, 0), (3, 15)])
