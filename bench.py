@@ -56,11 +56,35 @@ KERNEL_NAMES = {"fwd": "fwd32_kernel", "dq": "dq32_kernel", "dkv": "dkv32_kernel
 COPY_BYTES = 1 << 30
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments, whitespace runs collapsed (string literals kept)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            i = text.find("*/", i + 2)
+            i = n if i < 0 else i + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout do not change it)."""
     h = hashlib.sha256()
     for p in sorted((ROOT / "exact_attention_forward_amd" / "csrc").glob("*")):
         h.update(p.name.encode())
-        h.update(p.read_bytes())
+        h.update(_code_only(p.read_text()).encode())
     return h.hexdigest()[:16]
 
 

@@ -31,7 +31,8 @@ namespace fa {
 // tile, key block) pairs: the last key block of a tile fetches the first key
 // block of the workgroup's next tile, and requests the next tile's Q, dO (and
 // O) rows as soon as its own S and dP products no longer need the current
-// ones, so a new tile starts without waiting for its first block or rows.
+// ones (under the causal mask; without it, right after that block, where
+// fewer values are live), so a new tile starts with its first block in LDS.
 template <int HD, bool CAUSAL, int PREC, int NW, int BC, bool FUSE_D>
 __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs a) {
   constexpr int NT = NW * 64;
