@@ -23,6 +23,14 @@ GPU outputs with it.
 ``--counters`` runs a minimal program for rocprofv3 --pmc: a float32 copy of
 known size (the calibration kernel), then a few steps.
 
+``--configs`` reports every workload instead (tiny, ragged, GPT-2-medium
+float32 and bfloat16, long context): parity of sampled heads against the
+float64 oracle first, then forward, backward and forward+backward each timed
+over 9 runs after one warm-up (median and min, HIP events on the launch
+stream, after ~50 ms of untimed steps to settle the clock), and the oracle's
+time on one head extrapolated to the whole workload.  One JSON line per
+workload, then a summary line.
+
 ``--lab`` runs the lab of the fused-attention lesson instead: one head, no
 mask, float32 inputs uniform in [-2, 2), N in {256, ..., 4096}, d in {16, 64};
 for the fused forward, the unfused three-kernel forward, the no-rescale
@@ -110,6 +118,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="minimal run for rocprofv3 counter collection")
     ap.add_argument("--lab", action="store_true", help="fused vs unfused lab of the lesson (one head, float32)")
+    ap.add_argument("--configs", action="store_true", help="time and check every workload, not only the bench one")
     return ap.parse_args()
 
 
@@ -128,6 +137,8 @@ def main() -> int:
 
     if args.lab:
         return lab(args)
+    if args.configs:
+        return configs(args)
 
     case = I.gpt2m_case(I.BF16)
     B, H, T, hd = case.B, case.H, case.T, case.hd
@@ -276,6 +287,126 @@ def lab(args) -> int:
                       "warmup": 1, "statistic": "median ms (HIP events)", "device": torch.cuda.get_device_name(dev),
                       "rows": rows} if not args.counters else {"lab_counters_run": "done"}), flush=True)
     return 0
+
+
+PEAK_F32_MATRIX_TFLOPS = 157.3  # MI355X dense float32 MFMA
+
+
+def device_label(dev) -> dict:
+    """Device name, architecture, HIP version and the peak engine clock HIP reports."""
+    import ctypes
+
+    import torch
+
+    prop = torch.cuda.get_device_properties(dev)
+    clock_khz = None
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, dev.index or 0) == 0:  # hipDeviceAttributeClockRate
+            clock_khz = v.value
+    except OSError:  # pragma: no cover
+        pass
+    return {"device": prop.name, "arch": prop.gcnArchName, "hip": torch.version.hip, "cus": prop.multi_processor_count,
+            "peak_clock_mhz": clock_khz / 1000 if clock_khz else None}
+
+
+def configs(args) -> int:
+    """Every workload: sampled parity, then forward / backward / total times and the oracle's time."""
+    import numpy as np
+    import torch
+
+    import exact_attention_forward_amd as fa
+    from exact_attention_forward_amd import api
+    from exact_attention_forward_amd import inputs as I
+    from oracle import attention as oracle
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    work = [("C0", I.tiny_case(False), fa.FA_PREC_DEFAULT), ("C0", I.tiny_case(True), fa.FA_PREC_DEFAULT)]
+    work += [("C1", c, fa.FA_PREC_DEFAULT) for c in I.ragged_cases()]
+    work += [("C2", lambda: I.gpt2m_case(I.F32), fa.FA_PREC_DEFAULT),
+             ("C3", lambda: I.gpt2m_case(I.BF16), fa.FA_PREC_BF16),
+             ("C4", I.long_case, fa.FA_PREC_BF16X2)]
+    label = device_label(dev)
+    summary = []
+    for cfg, case, prec in work:
+        if callable(case):
+            case = case()
+        B, H, T, hd = case.B, case.H, case.T, case.hd
+        up = (lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)) \
+            if case.dtype == I.BF16 else (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+        q, k, v, do = (up(getattr(case, n)) for n in ("q", "k", "v", "do"))
+        o, lse = api.forward(q, k, v, case.scale, case.causal, prec)
+        dq, dk, dv, delta = api.backward(q, k, v, o, lse, do, case.scale, case.causal, prec)
+        torch.cuda.synchronize()
+        # parity of sampled heads (every head of the small workloads), timing the oracle on the first
+        heads = [(b, h) for b in range(B) for h in range(H)]
+        if len(heads) > 4:
+            heads = [heads[0], heads[len(heads) // 3], heads[2 * len(heads) // 3], heads[-1]]
+        worst, t_oracle = {}, None
+        for b, h in heads:
+            qh, kh, vh, dh = (case.head_f64(n, b, h) for n in ("q", "k", "v", "do"))
+            t0 = time.perf_counter()
+            O, L, _ = oracle.head_forward(qh, kh, vh, case.scale, case.causal)
+            dQ, dK, dV, _ = oracle.head_backward(qh, kh, vh, dh, case.scale, case.causal)
+            if t_oracle is None:
+                t_oracle = time.perf_counter() - t0
+            for n, got, ref in (("O", o[b, :, h], O), ("L", lse[b, h], L), ("dQ", dq[b, :, h], dQ),
+                                ("dK", dk[b, :, h], dK), ("dV", dv[b, :, h], dV)):
+                worst[n] = max(worst.get(n, 0.0), float(np.abs(got.cpu().numpy().astype(np.float64) - ref).max()))
+        tol = 2e-2 if case.dtype == I.BF16 else 2e-5
+        ok = all(e <= tol for e in worst.values())
+        dt = {I.F32: fa.FA_F32, I.BF16: fa.FA_BF16}[case.dtype]
+
+        def fwd():
+            fa.check(fa.fa_forward(q, k, v, o, lse, B, H, T, hd, case.scale, int(case.causal),
+                                   dt, prec, stream))
+
+        def bwd():
+            fa.check(fa.fa_backward(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, T, hd, case.scale,
+                                    int(case.causal), dt, prec, stream))
+
+        def both():
+            fwd()
+            bwd()
+
+        t_end = time.perf_counter() + 0.05  # settle the clock
+        while time.perf_counter() < t_end:
+            both()
+            torch.cuda.synchronize()
+        times = {}
+        for name, fn in (("fwd", fwd), ("bwd", bwd), ("total", both)):
+            fn()  # warm-up
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(9):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ts.sort()
+            times[name] = {"median_ms": round(ts[4], 5), "min_ms": round(ts[0], 5)}
+        pairs = B * H * (T * T / 2 if case.causal else T * T)
+        counted = 14 * hd * pairs
+        tflops = counted / (times["total"]["median_ms"] * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if case.dtype == I.BF16 else PEAK_F32_MATRIX_TFLOPS
+        rec = {"config": cfg, "workload": case.name, "B": B, "H": H, "T": T, "hd": hd, "dtype": case.dtype,
+               "causal": bool(case.causal), "precision": int(prec), "counted_gflop": round(counted / 1e9, 6),
+               "times": times, "tflops": round(tflops, 3), "frac_of_peak": round(tflops / peak, 4),
+               "peak_tflops": peak, "parity": {"heads": len(heads), "tol": tol, "ok": ok,
+                                               "max_abs_err": {n: float(f"{e:.3e}") for n, e in worst.items()}},
+               "oracle_s_per_head": round(t_oracle, 4), "oracle_s_est": round(t_oracle * B * H, 2)}
+        print(json.dumps(rec), flush=True)
+        summary.append(rec)
+        del q, k, v, do, o, lse, dq, dk, dv, delta, case
+        torch.cuda.empty_cache()
+    print(json.dumps({"configs": len(summary), "all_parity_ok": all(r["parity"]["ok"] for r in summary),
+                      "reps": 9, "warmup": 1, "statistic": "median and min ms (HIP events)",
+                      "oracle_threads": os.cpu_count(), **label}), flush=True)
+    return 0 if all(r["parity"]["ok"] for r in summary) else 1
 
 
 def cpu_baseline(case, out, budget_s: float):

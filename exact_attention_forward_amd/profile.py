@@ -19,6 +19,7 @@ Usage (from the repository root, on the machine where the databases are)::
     python -m exact_attention_forward_amd.profile util DB
     python -m exact_attention_forward_amd.profile report TRACE_DB FETCH_DB WRITE_DB UTIL_DB OUT_DIR HASH
     python -m exact_attention_forward_amd.profile lab LAB_JSON_LOG FETCH_DB WRITE_DB OUT_MD
+    python -m exact_attention_forward_amd.profile configs CONFIGS_LOG OUT_MD
 
 ``report`` writes the Markdown summaries and ``traffic.json`` of the causal
 B64 H16 T1024 hd64 bfloat16 workload into OUT_DIR; HASH is the kernel source
@@ -302,9 +303,49 @@ def lab_report(lab_log: str, fetch_db: str, write_db: str, out_md: str) -> None:
     Path(out_md).write_text("\n".join(lines) + "\n")
 
 
+def configs_report(log_path, out_md) -> None:
+    """Markdown table of a ``bench.py --configs`` log (one JSON line per workload, then a summary line)."""
+    recs, summary = [], {}
+    for line in Path(log_path).read_text().splitlines():
+        if line.startswith('{"config"'):
+            recs.append(json.loads(line))
+        elif line.startswith('{"configs"'):
+            summary = json.loads(line)
+    lines = ["# Every workload: parity, forward / backward times and the oracle's time (MI355X)", "",
+             "Command (from the repository root on the GPU box):", "",
+             "    python bench.py --configs > gpurun_out/configs.log",
+             "    python -m exact_attention_forward_amd.profile configs gpurun_out/configs.log OUT_MD", "",
+             f"Device: {summary.get('device')} ({summary.get('arch')}, {summary.get('cus')} CUs, peak engine clock "
+             f"{summary.get('peak_clock_mhz')} MHz as HIP reports it), HIP {summary.get('hip')}; oracle on "
+             f"{summary.get('oracle_threads')} host threads.  Each of forward, backward and forward + backward is "
+             "timed over 9 runs after one warm-up (HIP events on the launch stream, after ~50 ms of untimed steps); "
+             "the table gives the median and, in brackets, the minimum.  TFLOP/s count 14 hd flops per visible "
+             "(query, key) pair over the median total; the fraction is of the dense bf16 matrix peak (2500 TFLOP/s) "
+             "for bfloat16 inputs and of the float32 matrix peak (157.3 TFLOP/s) for float32 inputs.  Parity: max "
+             "abs error over O, L, dQ, dK, dV of the checked heads against the float64 oracle (every head of the "
+             "small workloads, four spread heads of the large ones).  Oracle: float64 NumPy forward + backward of "
+             "the first checked head, times the number of heads.", "",
+             "| config | workload | B H T hd | dtype | causal | prec | GFLOP | fwd ms | bwd ms | total ms | TFLOP/s | "
+             "% peak | parity (max err / tol) | oracle s/head | oracle s (all heads) |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in recs:
+        t = r["times"]
+        cell = lambda k: f"{t[k]['median_ms']:.4f} ({t[k]['min_ms']:.4f})"
+        err = max(r["parity"]["max_abs_err"].values())
+        lines.append(f"| {r['config']} | {r['workload']} | {r['B']} {r['H']} {r['T']} {r['hd']} | {r['dtype']} | "
+                     f"{'yes' if r['causal'] else 'no'} | {r['precision']} | {r['counted_gflop']:.4g} | {cell('fwd')} | "
+                     f"{cell('bwd')} | {cell('total')} | {r['tflops']:.2f} | {100 * r['frac_of_peak']:.2f} | "
+                     f"{err:.2e} / {r['parity']['tol']:.0e} {'ok' if r['parity']['ok'] else 'FAIL'} | "
+                     f"{r['oracle_s_per_head']:.4f} | {r['oracle_s_est']:.2f} |")
+    lines += ["", "The tiny and ragged workloads are launch-bound (a few microseconds per kernel); they are "
+              "correctness cases.  The precision column is the fa_precision code (0 default, 1 bf16 operands, 2 "
+              "split bf16 operands)."]
+    Path(out_md).write_text("\n".join(lines) + "\n")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab"))
+    ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab", "configs"))
     ap.add_argument("db", nargs="+")
     a = ap.parse_args(argv)
     if a.what == "trace":
@@ -315,6 +356,8 @@ def main(argv=None) -> int:
         print(json.dumps(util(a.db[0]), indent=1))
     elif a.what == "lab":
         lab_report(*a.db[:4])
+    elif a.what == "configs":
+        configs_report(*a.db[:2])
     else:
         report(*a.db[:6])
     return 0
