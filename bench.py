@@ -21,7 +21,8 @@ sample of the same workload (whole heads), and compares those heads of the
 GPU outputs with it.
 
 ``--counters`` runs a minimal program for rocprofv3 --pmc: a float32 copy of
-known size (the calibration kernel), then a few steps.
+known size (the calibration kernel), then a few steps (of the bench workload,
+or of each workload ``--workloads`` lists).
 
 ``--configs`` reports every workload instead (tiny, ragged, GPT-2-medium
 float32 and bfloat16, long context): parity of sampled heads against the
@@ -117,6 +118,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true", help="minimal run for rocprofv3 counter collection")
+    ap.add_argument("--workloads", default="C3",
+                    help="with --counters: comma-separated workloads to step (C2 f32, C3 bf16, C4 long bf16)")
     ap.add_argument("--lab", action="store_true", help="fused vs unfused lab of the lesson (one head, float32)")
     ap.add_argument("--configs", action="store_true", help="time and check every workload, not only the bench one")
     return ap.parse_args()
@@ -174,10 +177,16 @@ def main() -> int:
         for _ in range(3):
             y.copy_(x)
         torch.cuda.synchronize()
-        for _ in range(3):
-            step()
-        torch.cuda.synchronize()
-        print(json.dumps({"counters_run": "done", "copy_bytes": COPY_BYTES}), flush=True)
+        del x, y
+        names = [w.strip() for w in args.workloads.split(",") if w.strip()]
+        for name in names:
+            if name == "C3":
+                for _ in range(3):
+                    step()
+                torch.cuda.synchronize()
+            else:
+                counter_steps(name)
+        print(json.dumps({"counters_run": "done", "copy_bytes": COPY_BYTES, "workloads": names}), flush=True)
         return 0
 
     for _ in range(args.warmup):
@@ -290,6 +299,35 @@ def lab(args) -> int:
 
 
 PEAK_F32_MATRIX_TFLOPS = 157.3  # MI355X dense float32 MFMA
+
+
+def counter_steps(name: str, steps: int = 2) -> None:
+    """A few forward + backward steps of workload C2 (float32) or C4 (long context) for a counter run."""
+    import numpy as np
+    import torch
+
+    import exact_attention_forward_amd as fa
+    from exact_attention_forward_amd import inputs as I
+
+    case, prec = {"C2": (lambda: I.gpt2m_case(I.F32), fa.FA_PREC_DEFAULT),
+                  "C4": (I.long_case, fa.FA_PREC_BF16X2)}[name]
+    case = case()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    B, H, T, hd = case.B, case.H, case.T, case.hd
+    up = (lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)) \
+        if case.dtype == I.BF16 else (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+    dt = fa.FA_BF16 if case.dtype == I.BF16 else fa.FA_F32
+    q, k, v, do = (up(getattr(case, n)) for n in ("q", "k", "v", "do"))
+    f32 = lambda *s: torch.empty(s, device=dev, dtype=torch.float32)
+    o, lse, dq, dk, dv, delta = f32(B, T, H, hd), f32(B, H, T), f32(B, T, H, hd), f32(B, T, H, hd), \
+        f32(B, T, H, hd), f32(B, H, T)
+    for _ in range(steps):
+        fa.check(fa.fa_forward(q, k, v, o, lse, B, H, T, hd, case.scale, 1, dt, prec, stream))
+        fa.check(fa.fa_backward_dq_delta(q, k, v, o, lse, do, dq, delta, B, H, T, hd, case.scale, 1, dt, prec,
+                                         stream))
+        fa.check(fa.fa_backward_dkv(q, k, v, lse, do, delta, dk, dv, B, H, T, hd, case.scale, 1, dt, prec, stream))
+    torch.cuda.synchronize()
 
 
 def device_label(dev) -> dict:

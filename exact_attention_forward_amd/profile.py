@@ -20,6 +20,7 @@ Usage (from the repository root, on the machine where the databases are)::
     python -m exact_attention_forward_amd.profile report TRACE_DB FETCH_DB WRITE_DB UTIL_DB OUT_DIR HASH
     python -m exact_attention_forward_amd.profile lab LAB_JSON_LOG FETCH_DB WRITE_DB OUT_MD
     python -m exact_attention_forward_amd.profile configs CONFIGS_LOG OUT_MD
+    python -m exact_attention_forward_amd.profile traffic_all FETCH_DB WRITE_DB REQ_DB OUT_MD
 
 ``report`` writes the Markdown summaries and ``traffic.json`` of the causal
 B64 H16 T1024 hd64 bfloat16 workload into OUT_DIR; HASH is the kernel source
@@ -303,6 +304,124 @@ def lab_report(lab_log: str, fetch_db: str, write_db: str, out_md: str) -> None:
     Path(out_md).write_text("\n".join(lines) + "\n")
 
 
+# ---- every workload: requested bytes of each kernel's tile walk ----
+# (B, H, T, hd, input bytes, (forward query rows, key block), (dQ query rows,
+# key block), (dK/dV key rows, query block), D fused into the dQ kernel)
+WORKLOADS = {
+    "C2": dict(B=64, H=16, T=1024, hd=64, e=4, fwd=(128, 32), dq=(128, 32), dkv=(128, 32), fused_d=False),
+    "C3": dict(B=64, H=16, T=1024, hd=64, e=2, fwd=(128, 32), dq=(128, 64), dkv=(128, 64), fused_d=True),
+    "C4": dict(B=4, H=16, T=8192, hd=128, e=2, fwd=(128, 64), dq=(128, 64), dkv=(128, 64), fused_d=True),
+}
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def prefix_keys(N: int, br: int, bc: int) -> int:
+    """Key rows a causal query-tile walk requests per head: whole key blocks up to each tile's last row."""
+    return sum((_cdiv(min((t + 1) * br, N), bc)) * bc for t in range(_cdiv(N, br)))
+
+
+def suffix_rows(N: int, bk: int, bq: int) -> int:
+    """Query rows a causal key-tile walk requests per head: whole query blocks from the tile's first key."""
+    nqb = _cdiv(N, bq)
+    return sum((nqb - (t * bk) // bq) * bq for t in range(_cdiv(N, bk)))
+
+
+def kernel_model(wl: str, fam: str) -> dict:
+    """Requested (L2) and compulsory bytes per launch of one kernel of a causal workload."""
+    w = WORKLOADS[wl]
+    N, d, e, heads = w["T"], w["hd"], w["e"], w["B"] * w["H"]
+    nd = N * d
+    if fam in ("fwd32_kernel", "fwd_kernel"):
+        req_r = nd * e + 2 * d * e * prefix_keys(N, *w["fwd"])
+        comp_r, wr = 3 * nd * e, 4 * nd + 4 * N
+    elif fam in ("dq32_kernel", "dq_kernel"):
+        extra = 4 * nd + 4 * N if w["fused_d"] else 8 * N  # O and L (D computed) or L and D
+        req_r = 2 * nd * e + extra + 2 * d * e * prefix_keys(N, *w["dq"])
+        comp_r = 4 * nd * e + extra
+        wr = 4 * nd + (4 * N if w["fused_d"] else 0)
+    elif fam in ("dkv32_kernel", "dkv_kernel"):
+        req_r = 2 * nd * e + (2 * d * e + 8) * suffix_rows(N, *w["dkv"])
+        comp_r, wr = 4 * nd * e + 8 * N, 8 * nd
+    elif fam == "delta_kernel":
+        req_r = comp_r = 4 * nd + nd * e
+        wr = 4 * N
+    else:
+        raise KeyError(fam)
+    return {"req_read": req_r * heads, "comp_read": comp_r * heads, "write": wr * heads,
+            "pairs": heads * N * N / 2}
+
+
+def workload_of(kernel: str) -> str | None:
+    """C2 (float32 kernels), C3 (hd 64 bf16) or C4 (hd 128 bf16) from the template arguments."""
+    s = short_name(kernel)
+    if "<" not in s:
+        return None
+    first = s.split("<", 1)[1].split(",")[0].strip()
+    if first == "float":
+        return "C2"
+    return {"64": "C3", "128": "C4"}.get(first)
+
+
+def traffic_all_report(fetch_db, write_db, req_db, out_md) -> None:
+    """HBM and L2 bytes of every kernel of C2, C3, C4 against the tile-walk requests and compulsory bytes."""
+    f, w, r = counters(fetch_db), counters(write_db), counters(req_db)
+    copy = 1 << 30
+
+    def copy_val(cs, cn):
+        for k, v in cs.items():
+            if COPY_KERNEL in k and cn in v:
+                return max(v[cn])
+        raise RuntimeError(f"no {COPY_KERNEL} dispatch with {cn}")
+
+    rs, ws = copy / 1024 / copy_val(f, "FETCH_SIZE"), copy / 1024 / copy_val(w, "WRITE_SIZE")
+    l2r, l2w = copy / copy_val(r, "TCP_TCC_READ_REQ_sum"), copy / copy_val(r, "TCP_TCC_WRITE_REQ_sum")
+    durs = {}
+    c = sqlite3.connect(req_db)
+    for name, dur in c.execute("select kernel_name, duration from counters_collection"):
+        durs.setdefault(name, set()).add(float(dur))
+    rows = []
+    for k in sorted(set(f) | set(w) | set(r), key=lambda x: (workload_of(x) or "", short_name(x))):
+        fam, wl = family(k), workload_of(k)
+        if fam is None or wl is None:
+            continue
+        m = kernel_model(wl, fam)
+        hr = mean(f.get(k, {}).get("FETCH_SIZE", [])) * 1024 * rs
+        hw = mean(w.get(k, {}).get("WRITE_SIZE", [])) * 1024 * ws
+        lr = mean(r.get(k, {}).get("TCP_TCC_READ_REQ_sum", [])) * l2r
+        lw = mean(r.get(k, {}).get("TCP_TCC_WRITE_REQ_sum", [])) * l2w
+        tr = mean(r.get(k, {}).get("SQ_INSTS_VALU_TRANS_F32", [])) * 64
+        rows.append((wl, short_name(k), m, hr, hw, lr, lw, tr))
+    lines = ["# L2 requests and HBM bytes of every kernel against its tile walk (MI355X)", "",
+             "Commands (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+             "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/all_fetch -o f -- python3 bench.py --counters "
+             "--workloads C2,C3,C4",
+             "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/all_write -o w -- python3 bench.py --counters "
+             "--workloads C2,C3,C4",
+             "    rocprofv3 --pmc TCP_TCC_READ_REQ_sum TCP_TCC_WRITE_REQ_sum SQ_INSTS_VALU_TRANS_F32 "
+             "-d gpurun_out/all_req -o r -- python3 bench.py --counters --workloads C2,C3,C4",
+             "    python -m exact_attention_forward_amd.profile traffic_all F_DB W_DB R_DB OUT_MD", "",
+             f"Calibration on a 1 GiB device copy: HBM reads x{rs:.4f}, writes x{ws:.4f}; one L1-to-L2 read "
+             f"request = {l2r:.1f} B, one write request = {l2w:.1f} B.  Requested = the bytes the kernel's tile "
+             "walk asks for (every K/V block up to each query tile's last row, every Q/dO block from each key "
+             "tile's first row, whole blocks, plus the tile's own rows and outputs); compulsory = every tensor "
+             "once.  Transcendentals: executed v_exp/v_log/v_rcp lanes (SQ_INSTS_VALU_TRANS_F32 x 64) per causal "
+             "(query, key) pair (B H T^2 / 2).", "",
+             "| workload | kernel | requested read MB | L2 read MB (/req) | HBM read MB (/compulsory) | "
+             "write MB (model) | L2 write MB | HBM write MB | transcendentals / pair |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for wl, name, m, hr, hw, lr, lw, tr in rows:
+        lines.append(f"| {wl} | `{name}` | {m['req_read'] / 1e6:.1f} | {lr / 1e6:.1f} ({lr / m['req_read']:.2f}) | "
+                     f"{hr / 1e6:.1f} ({hr / m['comp_read']:.2f}) | {m['write'] / 1e6:.1f} | {lw / 1e6:.1f} | "
+                     f"{hw / 1e6:.1f} | {tr / m['pairs']:.3f} |")
+    lines += ["", "A ratio near 1 in the L2 column says the kernel asks for what its walk needs and no more "
+              "(clamped tail rows and LDS staging make it slightly above); the HBM column says how much of "
+              "that L2 absorbs (K/V and Q/dO blocks shared by the tiles of one head stay in the XCD's L2)."]
+    Path(out_md).write_text("\n".join(lines) + "\n")
+
+
 def configs_report(log_path, out_md) -> None:
     """Markdown table of a ``bench.py --configs`` log (one JSON line per workload, then a summary line)."""
     recs, summary = [], {}
@@ -345,7 +464,7 @@ def configs_report(log_path, out_md) -> None:
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab", "configs"))
+    ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab", "configs", "traffic_all"))
     ap.add_argument("db", nargs="+")
     a = ap.parse_args(argv)
     if a.what == "trace":
@@ -358,6 +477,8 @@ def main(argv=None) -> int:
         lab_report(*a.db[:4])
     elif a.what == "configs":
         configs_report(*a.db[:2])
+    elif a.what == "traffic_all":
+        traffic_all_report(*a.db[:4])
     else:
         report(*a.db[:6])
     return 0
