@@ -1,0 +1,48 @@
+"""Host logic of the counter summaries: the tile-walk request model and the kernel-name parsing."""
+import itertools
+
+import pytest
+
+from exact_attention_forward_amd import profile as P
+
+
+def brute_prefix(N, br, bc):
+    # every key block a causal query tile walks: blocks whose first key is <= the tile's last row
+    total = 0
+    for t in range(-(-N // br)):
+        last = min((t + 1) * br, N) - 1
+        total += sum(bc for j0 in range(0, N, bc) if j0 <= last)
+    return total
+
+
+def brute_suffix(N, bk, bq):
+    # every query block a causal key tile walks: blocks whose last row reaches the tile's first key
+    total = 0
+    for t in range(-(-N // bk)):
+        first = t * bk
+        total += sum(bq for q0 in range(0, N, bq) if q0 + bq - 1 >= first)
+    return total
+
+
+@pytest.mark.parametrize("N,a,b", list(itertools.product([1, 31, 64, 300, 1024], [64, 128], [32, 64])))
+def test_walk_counts_match_enumeration(N, a, b):
+    assert P.prefix_keys(N, a, b) == brute_prefix(N, a, b)
+    assert P.suffix_rows(N, a, b) == brute_suffix(N, a, b)
+
+
+def test_bf16_forward_requests_match_closed_form():
+    # causal forward at B64 H16 T1024 hd64, 128-row query tiles: per head Nd + (G+1) N d elements
+    # are read (Q once, the K and V prefix of G = 8 tiles), 2 bytes each
+    m = P.kernel_model("C3", "fwd32_kernel")
+    N, d, G, heads = 1024, 64, 8, 64 * 16
+    assert m["req_read"] == (N * d + (G + 1) * N * d) * 2 * heads
+    assert m["comp_read"] == 3 * N * d * 2 * heads
+    assert m["write"] == (4 * N * d + 4 * N) * heads
+
+
+def test_kernel_names_map_to_workloads():
+    assert P.workload_of("void fa::fwd32_kernel<64, true, 0, 2, 32, 2>(fa::FwdArgs)") == "C3"
+    assert P.workload_of("void fa::dkv32_kernel<128, true, 1, 4, 64>(fa::BwdArgs)") == "C4"
+    assert P.workload_of("void fa::dq_kernel<float, 64, true, 0, 4, 2, 32, false>(fa::BwdArgs)") == "C2"
+    assert P.workload_of("__amd_rocclr_copyBuffer") is None
+    assert P.family("void fa::delta_kernel<float, 64>(fa::BwdArgs)") == "delta_kernel"
