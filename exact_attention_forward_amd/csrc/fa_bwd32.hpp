@@ -1,4 +1,4 @@
-// bfloat16 backward kernels on 32x32 MFMA tiles.
+// 16-bit (bfloat16 or IEEE half) backward kernels on 32x32 MFMA tiles.
 //
 // Same mathematics and ownership as dq_kernel / dkv_kernel ("Flash Attention
 // 2 -- backward pass notes", sections "The math (FA2 backward with
@@ -33,7 +33,7 @@ namespace fa {
 // O) rows as soon as its own S and dP products no longer need the current
 // ones (under the causal mask; without it, right after that block, where
 // fewer values are live), so a new tile starts with its first block in LDS.
-template <int HD, bool CAUSAL, int PREC, int NW, int BC, bool FUSE_D>
+template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int BC, bool FUSE_D>
 __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
@@ -41,6 +41,7 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs
   constexpr int NDT = HD / 32;
   constexpr int NKS = HD / 16;
   constexpr int NKT = BC / 32;
+  using V8 = typename Frag32<TIn>::V;
   static_assert(HD % 32 == 0 && BC % 32 == 0, "tile shape");
   static_assert(2 * 2 * BC * LD * 2 <= 160 * 1024, "LDS budget");
 
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs
 
   // Rows of this lane: Q and dO fragments, O for D, raw L (and D).  Rows past T
   // read row T-1; their results are never stored.
-  bf16x8 qf[NKS], gf[NKS];
+  V8 qf[NKS], gf[NKS];
   f32x4 of[FUSE_D ? 2 * NKS : 1];
   float lraw = 0.f, draw = 0.f;
   auto load_rows = [&](int w) {
@@ -92,8 +93,8 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs
     const int rc = min(item_i0(w) + wave * 32 + n, T - 1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(Qg + bs + (size_t)rc * rs + 16 * ks + 8 * h);
-      gf[ks] = *reinterpret_cast<const bf16x8*>(Gg + bs + (size_t)rc * rs + 16 * ks + 8 * h);
+      qf[ks] = *reinterpret_cast<const V8*>(Qg + bs + (size_t)rc * rs + 16 * ks + 8 * h);
+      gf[ks] = *reinterpret_cast<const V8*>(Gg + bs + (size_t)rc * rs + 16 * ks + 8 * h);
       if (FUSE_D) {
         // lane (n, h) holds dO[row][16 ks + 8h .. +7]; its partner (n, 1-h) the rest
         of[2 * ks] = *reinterpret_cast<const f32x4*>(a.o + bs + (size_t)rc * rs + 16 * ks + 8 * h);
@@ -152,8 +153,8 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
           if (live(kt)) {
-            s[kt] = mma32(ld_row32(cK, LD, 32 * kt, 16 * ks, n, h), qf[ks], s[kt]);
-            dp[kt] = mma32(ld_row32(cV, LD, 32 * kt, 16 * ks, n, h), gf[ks], dp[kt]);
+            s[kt] = mma32(ld_row32<V8>(cK, LD, 32 * kt, 16 * ks, n, h), qf[ks], s[kt]);
+            dp[kt] = mma32(ld_row32<V8>(cV, LD, 32 * kt, 16 * ks, n, h), gf[ks], dp[kt]);
           }
       if (next_rows >= 0) load_rows(next_rows);
 #pragma unroll
@@ -172,12 +173,12 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs
         if (live(kt)) {
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const bf16x8 bf = pack32(s[kt], st);
-            bf16x8 bl;
-            if (PREC == 1) bl = pack32_lo(s[kt], st);
+            const V8 bf = pack32<V8>(s[kt], st);
+            V8 bl;
+            if (PREC == 1) bl = pack32_lo<V8>(s[kt], st);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-              const bf16x8 af = ld_tr32(cK, LD, 32 * kt + 16 * st, 32 * dt, lane);
+              const V8 af = ld_tr32<V8>(cK, LD, 32 * kt + 16 * st, 32 * dt, lane);
               acc[dt] = mma32(af, bf, acc[dt]);
               if (PREC == 1) acc[dt] = mma32(af, bl, acc[dt]);
             }
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dq32_kernel(BwdArgs
 // workgroup's next tile), so a new tile starts with its first block already in
 // LDS.  The next tile's K and V fragments are requested before the finished
 // tile's dK and dV are stored, so waiting for them never waits for the stores.
-template <int HD, bool CAUSAL, int PREC, int NW, int BQ>
+template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int BQ>
 __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BK = NW * 32;
@@ -258,6 +259,7 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
   constexpr int NDT = HD / 32;
   constexpr int NKS = HD / 16;
   constexpr int NIT = BQ / 32;
+  using V8 = typename Frag32<TIn>::V;
   static_assert(HD % 32 == 0 && BQ % 32 == 0, "tile shape");
   static_assert(BQ <= NT, "one thread per query row fetches that row's L and D");
   static_assert(2 * 2 * BQ * LD * 2 + 2 * 2 * BQ * 4 <= 160 * 1024, "LDS budget");
@@ -316,14 +318,14 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
       sD[sb][tid] = live ? dnext : 0.f;
     }
   };
-  bf16x8 kf[NKS], vf[NKS];
+  V8 kf[NKS], vf[NKS];
   auto load_kv = [&](int w) {
     const size_t bs = item_base(w);
     const int c = (w % nkt) * BK + wave * 32 + n;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = ld_row_global32(Kg + bs, rs, c, T, 16 * ks, h);
-      vf[ks] = ld_row_global32(Vg + bs, rs, c, T, 16 * ks, h);
+      kf[ks] = ld_row_global32<V8>(Kg + bs, rs, c, T, 16 * ks, h);
+      vf[ks] = ld_row_global32<V8>(Vg + bs, rs, c, T, 16 * ks, h);
     }
   };
 
@@ -362,8 +364,8 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
         da = zero16();
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          sa = mma32(ld_row32(cQ, LD, 32 * it, 16 * ks, n, h), kf[ks], sa);
-          da = mma32(ld_row32(cG, LD, 32 * it, 16 * ks, n, h), vf[ks], da);
+          sa = mma32(ld_row32<V8>(cQ, LD, 32 * it, 16 * ks, n, h), kf[ks], sa);
+          da = mma32(ld_row32<V8>(cG, LD, 32 * it, 16 * ks, n, h), vf[ks], da);
         }
       };
       stage_a(0, s[0], dp[0]);
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
         if (it + 1 < NIT) stage_a(it + 1, s[(it + 1) & 1], dp[(it + 1) & 1]);
         // stage B: P = exp2(S c - L), dS = P (dP - D), packed for the products
         const int lim = lo - (q0 + 32 * it);
-        bf16x8 bp[2], bs[2], bpl[2], bsl[2];
+        V8 bp[2], bs[2], bpl[2], bsl[2];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int rr = 32 * it + 8 * bb + 4 * h;
@@ -391,11 +393,11 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          bp[st] = pack32(sc, st);
-          bs[st] = pack32(dc, st);
+          bp[st] = pack32<V8>(sc, st);
+          bs[st] = pack32<V8>(dc, st);
           if (PREC == 1) {
-            bpl[st] = pack32_lo(sc, st);
-            bsl[st] = pack32_lo(dc, st);
+            bpl[st] = pack32_lo<V8>(sc, st);
+            bsl[st] = pack32_lo<V8>(dc, st);
           }
         }
         // stage C
@@ -403,8 +405,8 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8 ga = ld_tr32(cG, LD, 32 * it + 16 * st, 32 * dt, lane);
-            const bf16x8 qa = ld_tr32(cQ, LD, 32 * it + 16 * st, 32 * dt, lane);
+            const V8 ga = ld_tr32<V8>(cG, LD, 32 * it + 16 * st, 32 * dt, lane);
+            const V8 qa = ld_tr32<V8>(cQ, LD, 32 * it + 16 * st, 32 * dt, lane);
             dv[dt] = mma32(ga, bp[st], dv[dt]);
             dk[dt] = mma32(qa, bs[st], dk[dt]);
             if (PREC == 1) {

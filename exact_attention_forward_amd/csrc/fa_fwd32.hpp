@@ -1,4 +1,4 @@
-// bfloat16 forward kernel on 32x32 MFMA tiles.
+// 16-bit (bfloat16 or IEEE half) forward kernel on 32x32 MFMA tiles.
 //
 // Same algorithm as fwd_kernel ("Flash Attention 2 -- forward pass notes",
 // section "Loop (per (b, h, Q-tile))"): online softmax over streamed K/V
@@ -16,8 +16,9 @@
 //    necessarily the exact row max: it is raised (and O, l rescaled) only when
 //    a block's max exceeds it by more than 2^8 in the exponential's units.
 //    The normalised result is the same for any reference (O = sum p v / sum p
-//    with the same p in both), and weights up to 2^8 stay far from overflow.
-//  * Row sums add the bfloat16 weights that enter the P V product (dot
+//    with the same p in both), and weights up to 2^8 stay far from overflow
+//    (in half precision too, whose largest finite value is 65504).
+//  * Row sums add the 16-bit weights that enter the P V product (dot
 //    products with (1, 1)), so O is normalised by exactly the weights used.
 //  * Blocks crossing the causal diagonal or the end of the sequence apply an
 //    element-wise -inf mask to the raw scores before the row max; sub-tiles
@@ -42,7 +43,8 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Adds the eight bfloat16 values of an operand fragment to two partial sums.
+// Adds the eight 16-bit values of an operand fragment to two partial sums
+// (one2 holds the pair (1, 1) in the fragment's format).
 // The pairs are taken with shufflevector: reinterpreting the fragment as four
 // 32-bit words before the dot products was mis-lowered by the compiler (the
 // same register fed every product).
@@ -52,6 +54,14 @@ __device__ __forceinline__ void sum8(bf16x8 v, unsigned one2, float& acc0, float
   acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), o, acc1, false);
   acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), o, acc0, false);
   acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), o, acc1, false);
+}
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void sum8(f16x8 v, unsigned one2, float& acc0, float& acc1) {
+  const f16x2 o = __builtin_bit_cast(f16x2, one2);
+  acc0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), o, acc0, false);
+  acc1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), o, acc1, false);
+  acc0 = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), o, acc0, false);
+  acc1 = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), o, acc1, false);
 }
 
 // Exponent headroom (base 2) before the reference max is raised.
@@ -76,7 +86,7 @@ __device__ __forceinline__ int subtile_row(int wave, int u) {
 #ifndef FA_FWD_WPE64
 #define FA_FWD_WPE64 2
 #endif
-template <int HD, bool CAUSAL, int PREC, int NW, int BC, int MS>
+template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int BC, int MS>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(HD <= 64 ? FA_FWD_WPE64 : 1, HD <= 64 ? FA_FWD_WPE64 : 1)))
 void fwd32_kernel(FwdArgs a) {
@@ -91,6 +101,7 @@ void fwd32_kernel(FwdArgs a) {
   static_assert(2 * 2 * BC * LD * 2 <= 160 * 1024, "LDS budget");
   static_assert(MS == 1 || MS == 2, "one or two sub-tiles per wave");
   using Copy = TileStream<HD, BC, NT>;
+  using V8 = typename Frag32<TIn>::V;
 
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][BC * LD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][BC * LD];
@@ -121,7 +132,7 @@ void fwd32_kernel(FwdArgs a) {
     const int i0 = qt * BR;
     const int nkb = CAUSAL ? ((min(i0 + BR, T) - 1) / BC + 1) : (T + BC - 1) / BC;
 
-    bf16x8 qf[MS][NKS];
+    V8 qf[MS][NKS];
     f32x16 oacc[MS][NDT];
     float mref[MS], ls0[MS], ls1[MS];
     int r0[MS], vis[MS], lastb[MS];
@@ -130,7 +141,7 @@ void fwd32_kernel(FwdArgs a) {
       r0[u] = i0 + subtile_row<NW, MS>(wave, u);
       const int row = r0[u] + n;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[u][ks] = ld_row_global32(Q, rs, row, T, 16 * ks, h);
+      for (int ks = 0; ks < NKS; ++ks) qf[u][ks] = ld_row_global32<V8>(Q, rs, row, T, 16 * ks, h);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[u][dt] = zero16();
       mref[u] = -INFINITY;
@@ -186,7 +197,7 @@ void fwd32_kernel(FwdArgs a) {
     };
     // P = exp2(s c2 - m) packed to bfloat16 (pk; the residual in pl for the
     // split precision), row sums updated.
-    auto softmax_exp = [&](int u, f32x16* s, bf16x8 (*pk)[2], bf16x8 (*pl)[2]) {
+    auto softmax_exp = [&](int u, f32x16* s, V8 (*pk)[2], V8 (*pl)[2]) {
       const float muse = mref[u] == -INFINITY ? 0.f : mref[u];
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
@@ -194,9 +205,9 @@ void fwd32_kernel(FwdArgs a) {
         for (int e = 0; e < 16; ++e) s[kt][e] = fast_exp2(fmaf(s[kt][e], c2, -muse));
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          pk[kt][st] = pack32(s[kt], st);
+          pk[kt][st] = pack32<V8>(s[kt], st);
           if (PREC == 0) sum8(pk[kt][st], one2, ls0[u], ls1[u]);
-          if (PREC == 1) pl[kt][st] = pack32_lo(s[kt], st);
+          if (PREC == 1) pl[kt][st] = pack32_lo<V8>(s[kt], st);
         }
         if (PREC == 1) {
 #pragma unroll
@@ -220,7 +231,7 @@ void fwd32_kernel(FwdArgs a) {
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
-          const bf16x8 kop = ld_row32(cK, LD, 32 * kt, 16 * ks, n, h);
+          const V8 kop = ld_row32<V8>(cK, LD, 32 * kt, 16 * ks, n, h);
 #pragma unroll
           for (int u = 0; u < MS; ++u)
             if (live[u]) s[u][kt] = mma32(kop, qf[u][ks], s[u][kt]);
@@ -228,17 +239,17 @@ void fwd32_kernel(FwdArgs a) {
       if (live[0]) softmax_max(0, s[0], j0, std::integral_constant<bool, S0 == 2>{});
       if constexpr (MS > 1)
         if (live[1]) softmax_max(1, s[1], j0, std::integral_constant<bool, S1 == 2>{});
-      bf16x8 vop[NKT][2][NDT];
+      V8 vop[NKT][2][NDT];
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) vop[kt][st][dt] = ld_tr32(cV, LD, 32 * kt + 16 * st, 32 * dt, lane);
+          for (int dt = 0; dt < NDT; ++dt) vop[kt][st][dt] = ld_tr32<V8>(cV, LD, 32 * kt + 16 * st, 32 * dt, lane);
 #pragma unroll
       for (int u = 0; u < MS; ++u) {
         if (!live[u]) continue;
-        bf16x8 pk[NKT][2], pl[NKT][2];
+        V8 pk[NKT][2], pl[NKT][2];
         softmax_exp(u, s[u], pk, pl);
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)

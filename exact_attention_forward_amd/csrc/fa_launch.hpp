@@ -97,17 +97,22 @@ inline long persistent_grid(K kernel, int threads, long items) {
 
 template <typename TIn>
 constexpr bool is_bf16 = std::is_same<TIn, bf16_t>::value;
+// 16-bit inputs run the 32x32 kernels
+template <typename TIn>
+constexpr bool is_16bit = std::is_same<TIn, bf16_t>::value || std::is_same<TIn, f16_t>::value;
 
 template <typename TIn, int HD, bool CAUSAL, int PREC, int CONTROL = kCtlNone>
 int run_fwd(const FwdArgs& a, hipStream_t s) {
   if constexpr (CONTROL != kCtlNone && is_bf16<TIn>) {
     return -3;  // the control variants are built for float32 and half inputs only
-  } else if constexpr (is_bf16<TIn>) {
+  } else if constexpr (CONTROL == kCtlNone && is_16bit<TIn>) {
     using C = TileCfg32<HD>;
-    auto* k = &fwd32_kernel<HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC, C::FWD_MS>;
+    auto* k = &fwd32_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC, C::FWD_MS>;
     constexpr int BR = C::FWD_NW * 32 * C::FWD_MS;
     const long items = (long)((a.T + BR - 1) / BR) * a.B * a.H;
-    hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::FWD_NW * 64, items)), dim3(C::FWD_NW * 64), 0, s, a);
+    FwdArgs b = a;
+    if constexpr (!is_bf16<TIn>) b.one2 = 0x3C003C00u;  // half pair (1, 1) for the row sums
+    hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::FWD_NW * 64, items)), dim3(C::FWD_NW * 64), 0, s, b);
     return launch_status();
   } else {
     using C = TileCfg<TIn, HD>;
@@ -130,9 +135,9 @@ int run_delta(const BwdArgs& a, hipStream_t s) {
 
 template <typename TIn, int HD, bool CAUSAL, int PREC, bool FUSE_D = false>
 int run_dq(const BwdArgs& a, hipStream_t s) {
-  if constexpr (is_bf16<TIn>) {
+  if constexpr (is_16bit<TIn>) {
     using C = TileCfg32<HD>;
-    auto* k = &dq32_kernel<HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC, FUSE_D>;
+    auto* k = &dq32_kernel<TIn, HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC, FUSE_D>;
     const long items = (long)((a.T + C::DQ_NW * 32 - 1) / (C::DQ_NW * 32)) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DQ_NW * 64, items)), dim3(C::DQ_NW * 64), 0, s, a);
     return launch_status();
@@ -151,9 +156,9 @@ int run_dq(const BwdArgs& a, hipStream_t s) {
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_dkv(const BwdArgs& a, hipStream_t s) {
-  if constexpr (is_bf16<TIn>) {
+  if constexpr (is_16bit<TIn>) {
     using C = TileCfg32<HD>;
-    auto* k = &dkv32_kernel<HD, CAUSAL, PREC, C::DKV_NW, C::DKV_BQ>;
+    auto* k = &dkv32_kernel<TIn, HD, CAUSAL, PREC, C::DKV_NW, C::DKV_BQ>;
     const long items = (long)((a.T + C::DKV_NW * 32 - 1) / (C::DKV_NW * 32)) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DKV_NW * 64, items)), dim3(C::DKV_NW * 64), 0, s, a);
     return launch_status();
@@ -213,7 +218,7 @@ int run_stage(int stage, const void* args, hipStream_t s) {
 
 template <typename TIn, int HD>
 int run_stage_hd(int stage, const void* args, bool causal, int prec, hipStream_t s) {
-  if constexpr (sizeof(TIn) == 2) {
+  if constexpr (is_bf16<TIn>) {  // the split operand exists for bfloat16 only
     if (prec == 1)
       return causal ? run_stage<TIn, HD, true, 1>(stage, args, s) : run_stage<TIn, HD, false, 1>(stage, args, s);
   }

@@ -1,4 +1,7 @@
-// 32x32 MFMA building blocks for the bfloat16 kernels (v_mfma_f32_32x32x16_bf16).
+// 32x32 MFMA building blocks for the 16-bit kernels (v_mfma_f32_32x32x16_bf16
+// and v_mfma_f32_32x32x16_f16).  Tiles in LDS and global memory are handled
+// as 16-bit bit patterns; the operand vector type V (bf16x8 or f16x8) decides
+// the product, the rounding of float results to operands, and nothing else.
 //
 // Lane l is split as n = l % 32 and h = l / 32.  Layouts:
 //   A (32 x 16): lane (n, h) holds row n, contraction indices 8h .. 8h+7
@@ -32,39 +35,73 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Operand vector of an input storage type, and its element type.
+template <typename TIn>
+struct Frag32;
+template <>
+struct Frag32<bf16_t> {
+  using V = bf16x8;
+  using E = __bf16;
+};
+template <>
+struct Frag32<f16_t> {
+  using V = f16x8;
+  using E = _Float16;
+};
+template <typename V>
+struct VecElem;
+template <>
+struct VecElem<bf16x8> {
+  using E = __bf16;
+};
+template <>
+struct VecElem<f16x8> {
+  using E = _Float16;
+};
 
 // X[row0 + n][k0 + 8h .. +7] from a row-major LDS tile.
-__device__ __forceinline__ bf16x8 ld_row32(const bf16_t* X, int ld, int row0, int k0, int n, int h) {
-  return *reinterpret_cast<const bf16x8*>(X + (row0 + n) * ld + k0 + 8 * h);
+template <typename V = bf16x8>
+__device__ __forceinline__ V ld_row32(const bf16_t* X, int ld, int row0, int k0, int n, int h) {
+  return *reinterpret_cast<const V*>(X + (row0 + n) * ld + k0 + 8 * h);
 }
 
 // A operand Y^T for one 16-long product step starting at row k0 of a
 // row-major LDS tile Y[k][m]: lane (n, h) receives Y[k][m0 + n] for
 // k = k0 + 4h + e (elements 0..3) and k = k0 + 8 + 4h + e (elements 4..7).
-__device__ __forceinline__ bf16x8 ld_tr32(const bf16_t* Y, int ld, int k0, int m0, int lane) {
+template <typename V = bf16x8>
+__device__ __forceinline__ V ld_tr32(const bf16_t* Y, int ld, int k0, int m0, int lane) {
   const int u = lane & 15, g = (lane >> 4) & 1, h = lane >> 5;
   const bf16_t* p = Y + (k0 + 4 * h + (u >> 2)) * ld + m0 + 16 * g + 4 * (u & 3);
   i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
   i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * ld));
   typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
   i16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, r);
+  return __builtin_bit_cast(V, r);
 }
 
-// B operand for product step s from a C tile (elements 8s .. 8s+7).
-__device__ __forceinline__ bf16x8 pack32(const f32x16& c, int s) {
-  bf16x8 r;
+// B operand for product step s from a C tile (elements 8s .. 8s+7), rounded
+// to nearest.
+template <typename V = bf16x8>
+__device__ __forceinline__ V pack32(const f32x16& c, int s) {
+  using E = typename VecElem<V>::E;
+  V r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)c[8 * s + e];
+  for (int e = 0; e < 8; ++e) r[e] = (E)c[8 * s + e];
   return r;
 }
-// Residual x - bf16(x) of the same elements, rounded to bfloat16.
-__device__ __forceinline__ bf16x8 pack32_lo(const f32x16& c, int s) {
-  bf16x8 r;
+// Residual x - round(x) of the same elements, rounded again.
+template <typename V = bf16x8>
+__device__ __forceinline__ V pack32_lo(const f32x16& c, int s) {
+  using E = typename VecElem<V>::E;
+  V r;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = c[8 * s + e];
-    r[e] = (__bf16)(x - (float)(__bf16)x);
+    r[e] = (E)(x - (float)(E)x);
   }
   return r;
 }
@@ -74,11 +111,12 @@ __device__ __forceinline__ int crow(int e, int h) { return 8 * (e >> 2) + 4 * h 
 
 // B operand (or A operand) straight from global memory: row `row` (zero if
 // past nrows), elements k0 + 8h .. +7.
-__device__ __forceinline__ bf16x8 ld_row_global32(const bf16_t* X, size_t ld, int row, int nrows, int k0, int h) {
-  if (row < nrows) return *reinterpret_cast<const bf16x8*>(X + (size_t)row * ld + k0 + 8 * h);
-  bf16x8 z;
+template <typename V = bf16x8>
+__device__ __forceinline__ V ld_row_global32(const bf16_t* X, size_t ld, int row, int nrows, int k0, int h) {
+  if (row < nrows) return *reinterpret_cast<const V*>(X + (size_t)row * ld + k0 + 8 * h);
+  V z;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
+  for (int e = 0; e < 8; ++e) z[e] = (typename VecElem<V>::E)0.f;
   return z;
 }
 
