@@ -1,4 +1,5 @@
-// IEEE half instantiations: head dims 64 and 128, on the 16x16 kernels.
+// IEEE half instantiations: head dims 64 and 128 (32x32 kernels; the softmax controls and the split
+// forward on the 16x16 kernels).
 #include "fa_launch.hpp"
 
 namespace fa {
