@@ -199,7 +199,7 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
     lines = [f"# Kernel trace: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
              "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, paths absolute):",
              "", "    rocprofv3 --kernel-trace --stats -d gpurun_out/prof_trace -o trace -- "
-             "python3 bench.py --no-cpu-baseline --steps 20 --warmup 5", "", trace_table(trace_db)]
+             "python3 bench.py --no-cpu-baseline --steps 20", "", trace_table(trace_db)]
     (out / "kernel_trace_gpt2m_bf16.md").write_text("\n".join(lines) + "\n")
 
     flops = {"fwd32_kernel": 4, "dq32_kernel": 6, "dkv32_kernel": 8}
