@@ -359,10 +359,13 @@ def workload_of(kernel: str) -> str | None:
     s = short_name(kernel)
     if "<" not in s:
         return None
-    first = s.split("<", 1)[1].split(",")[0].strip()
-    if first == "float":
+    args = [x.strip() for x in s.split("<", 1)[1].rstrip(">").split(",")]
+    if args[0] == "float":
         return "C2"
-    return {"64": "C3", "128": "C4"}.get(first)
+    hd = args[1] if args[0] in ("bf16_t", "f16_t") else args[0]
+    if args[0] == "f16_t":
+        return None
+    return {"64": "C3", "128": "C4"}.get(hd)
 
 
 def traffic_all_report(fetch_db, write_db, req_db, out_md) -> None:

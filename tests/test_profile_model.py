@@ -41,8 +41,9 @@ def test_bf16_forward_requests_match_closed_form():
 
 
 def test_kernel_names_map_to_workloads():
-    assert P.workload_of("void fa::fwd32_kernel<64, true, 0, 2, 32, 2>(fa::FwdArgs)") == "C3"
-    assert P.workload_of("void fa::dkv32_kernel<128, true, 1, 4, 64>(fa::BwdArgs)") == "C4"
+    assert P.workload_of("void fa::fwd32_kernel<fa::bf16_t, 64, true, 0, 2, 32, 2>(fa::FwdArgs)") == "C3"
+    assert P.workload_of("void fa::dkv32_kernel<fa::bf16_t, 128, true, 1, 4, 64>(fa::BwdArgs)") == "C4"
+    assert P.workload_of("void fa::dq32_kernel<fa::f16_t, 64, true, 0, 4, 64, true>(fa::BwdArgs)") is None
     assert P.workload_of("void fa::dq_kernel<float, 64, true, 0, 4, 2, 32, false>(fa::BwdArgs)") == "C2"
     assert P.workload_of("__amd_rocclr_copyBuffer") is None
     assert P.family("void fa::delta_kernel<float, 64>(fa::BwdArgs)") == "delta_kernel"
