@@ -25,7 +25,7 @@ known size (the calibration kernel), then a few steps (of the bench workload,
 or of each workload ``--workloads`` lists).
 
 ``--configs`` reports every workload instead (tiny, ragged, GPT-2-medium
-float32 and bfloat16, long context): parity of sampled heads against the
+float32, bfloat16 and IEEE half, long context): parity of sampled heads against the
 float64 oracle first, then forward, backward and forward+backward each timed
 over 9 runs after one warm-up (median and min, HIP events on the launch
 stream, after ~50 ms of untimed steps to settle the clock), and the oracle's
@@ -365,6 +365,7 @@ def configs(args) -> int:
     work += [("C1", c, fa.FA_PREC_DEFAULT) for c in I.ragged_cases()]
     work += [("C2", lambda: I.gpt2m_case(I.F32), fa.FA_PREC_DEFAULT),
              ("C3", lambda: I.gpt2m_case(I.BF16), fa.FA_PREC_BF16),
+             ("C3-f16", lambda: I.gpt2m_case(I.F16), fa.FA_PREC_DEFAULT),
              ("C4", I.long_case, fa.FA_PREC_BF16X2)]
     label = device_label(dev)
     summary = []
@@ -372,8 +373,9 @@ def configs(args) -> int:
         if callable(case):
             case = case()
         B, H, T, hd = case.B, case.H, case.T, case.hd
-        up = (lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)) \
-            if case.dtype == I.BF16 else (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+        t16 = {I.BF16: torch.bfloat16, I.F16: torch.float16}.get(case.dtype)
+        up = (lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(t16).to(dev)) \
+            if t16 is not None else (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev))
         q, k, v, do = (up(getattr(case, n)) for n in ("q", "k", "v", "do"))
         o, lse = api.forward(q, k, v, case.scale, case.causal, prec)
         dq, dk, dv, delta = api.backward(q, k, v, o, lse, do, case.scale, case.causal, prec)
@@ -393,9 +395,9 @@ def configs(args) -> int:
             for n, got, ref in (("O", o[b, :, h], O), ("L", lse[b, h], L), ("dQ", dq[b, :, h], dQ),
                                 ("dK", dk[b, :, h], dK), ("dV", dv[b, :, h], dV)):
                 worst[n] = max(worst.get(n, 0.0), float(np.abs(got.cpu().numpy().astype(np.float64) - ref).max()))
-        tol = 2e-2 if case.dtype == I.BF16 else 2e-5
+        tol = 2e-5 if case.dtype == I.F32 else 2e-2
         ok = all(e <= tol for e in worst.values())
-        dt = {I.F32: fa.FA_F32, I.BF16: fa.FA_BF16}[case.dtype]
+        dt = {I.F32: fa.FA_F32, I.BF16: fa.FA_BF16, I.F16: fa.FA_F16}[case.dtype]
 
         def fwd():
             fa.check(fa.fa_forward(q, k, v, o, lse, B, H, T, hd, case.scale, int(case.causal),
@@ -430,7 +432,7 @@ def configs(args) -> int:
         pairs = B * H * (T * T / 2 if case.causal else T * T)
         counted = 14 * hd * pairs
         tflops = counted / (times["total"]["median_ms"] * 1e-3) / 1e12
-        peak = PEAK_BF16_TFLOPS if case.dtype == I.BF16 else PEAK_F32_MATRIX_TFLOPS
+        peak = PEAK_F32_MATRIX_TFLOPS if case.dtype == I.F32 else PEAK_BF16_TFLOPS  # fp16 dense = bf16 dense
         rec = {"config": cfg, "workload": case.name, "B": B, "H": H, "T": T, "hd": hd, "dtype": case.dtype,
                "causal": bool(case.causal), "precision": int(prec), "counted_gflop": round(counted / 1e9, 6),
                "times": times, "tflops": round(tflops, 3), "frac_of_peak": round(tflops / peak, 4),

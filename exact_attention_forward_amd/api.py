@@ -2,7 +2,7 @@
 
 torch supplies device memory and the current stream; every step of the
 computation runs in the HIP library.  Inputs are contiguous [B, T, H, hd]
-device tensors of dtype float32 or bfloat16; outputs are float32.
+device tensors of dtype float32, bfloat16 or float16; outputs are float32.
 """
 from __future__ import annotations
 
@@ -10,7 +10,7 @@ import math
 
 import torch
 
-from ._binding import (FA_BF16, FA_F32, FA_PREC_DEFAULT, check, fa_backward, fa_backward_delta, fa_backward_dkv,
+from ._binding import (FA_BF16, FA_F16, FA_F32, FA_PREC_DEFAULT, check, fa_backward, fa_backward_delta, fa_backward_dkv,
                        fa_backward_dq, fa_forward)
 
 
@@ -19,6 +19,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return FA_F32
     if t.dtype == torch.bfloat16:
         return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_F16
     raise TypeError(f"unsupported input dtype {t.dtype}")
 
 
