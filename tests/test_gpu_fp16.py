@@ -1,7 +1,8 @@
 """IEEE half inputs on the GPU, and the overflow of the softmax without its max.
 
 Parity: the forward and the backward with FA_F16 inputs against the float64
-oracle (max abs 2e-2, the 16-bit input bar), through the C ABI.
+oracle (max abs 2e-2, the 16-bit input bar), through the C ABI, on small shapes
+and on a ragged shape where every persistent workgroup walks several tiles.
 
 Overflow ("Lesson K23, fused attention", block ``overflow``): scores reaching
 ln 65520 = 11.09 are harmless for fa_forward, which subtracts the running max,
@@ -21,7 +22,7 @@ from exact_attention_forward_amd import inputs as I
 from oracle import attention as oracle
 from oracle import overflow
 
-from gpu_util import BF16_TOL, assert_within, full_errors, run_case, to_device
+from gpu_util import BF16_TOL, assert_within, full_errors, head_errors, run_case, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +37,22 @@ def test_f16_forward_backward(shape, causal):
     err = full_errors(c, run_case(c))
     print(f"[f16] {shape} causal={causal} " + " ".join(f"{k}={v:.2e}" for k, v in err.items()), flush=True)
     assert_within(err, BF16_TOL, c.name)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_f16_ragged_multi_item_sampled(causal):
+    # enough (tile, head) items that every persistent workgroup walks several
+    B, H, T, hd = 2, 128, 1000, 64
+    c = I.make_case("f16_multi_item", B, H, T, hd, I.F16, causal, 71)
+    out = run_case(c)
+    for n, t in out.items():
+        assert bool(torch.isfinite(t).all()), f"{n} has unwritten or non-finite elements"
+    worst = {}
+    for b, h in [(0, 0), (0, 37), (1, 64), (1, 127)]:
+        for n, e in head_errors(c, out, b, h).items():
+            worst[n] = max(worst.get(n, 0.0), e)
+    print(f"[f16 multi-item] causal={causal} " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()), flush=True)
+    assert_within(worst, BF16_TOL, c.name)
 
 
 def test_f16_splitkv():
