@@ -330,6 +330,26 @@ def counter_steps(name: str, steps: int = 2) -> None:
     torch.cuda.synchronize()
 
 
+def host_label() -> dict:
+    """Host CPU model, logical cores and the BLAS thread count the oracle runs with."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        import numpy  # noqa: F401  (loads the BLAS library the oracle's products use)
+        from threadpoolctl import threadpool_info
+
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = None
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "blas_threads": blas}
+
+
 def device_label(dev) -> dict:
     """Device name, architecture, HIP version and the peak engine clock HIP reports."""
     import ctypes
@@ -445,7 +465,7 @@ def configs(args) -> int:
         torch.cuda.empty_cache()
     print(json.dumps({"configs": len(summary), "all_parity_ok": all(r["parity"]["ok"] for r in summary),
                       "reps": 9, "warmup": 1, "statistic": "median and min ms (HIP events)",
-                      "oracle_threads": os.cpu_count(), **label}), flush=True)
+                      "oracle_threads": host_label()["blas_threads"], "host": host_label(), **label}), flush=True)
     return 0 if all(r["parity"]["ok"] for r in summary) else 1
 
 
@@ -455,12 +475,8 @@ def cpu_baseline(case, out, budget_s: float):
 
     from oracle import attention as oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    host = host_label()
+    threads = host["blas_threads"] or host["cpu_count"] or 1
     heads = [(b, h) for b in range(case.B) for h in range(case.H)]
     order = np.random.default_rng(0).permutation(len(heads))
     done, worst = [], {}
@@ -479,7 +495,8 @@ def cpu_baseline(case, out, budget_s: float):
     el = time.perf_counter() - t0
     flops = 14 * case.hd * case.T * case.T / 2 * len(done)
     base = {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(done)} of {case.B * case.H} heads (float64 NumPy, fwd+bwd per head), {el:.1f} s"}
+            "sample": f"{len(done)} of {case.B * case.H} heads (float64 NumPy, fwd+bwd per head), {el:.1f} s",
+            "cpu_model": host["cpu_model"]}
     parity = {"heads": len(done), "max_abs_err": {k: float(f"{v:.3e}") for k, v in worst.items()}, "tol": 2e-2,
               "ok": all(v <= 2e-2 for v in worst.values())}
     return base, parity

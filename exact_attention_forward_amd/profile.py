@@ -439,7 +439,8 @@ def configs_report(log_path, out_md) -> None:
              "    python -m exact_attention_forward_amd.profile configs gpurun_out/configs.log OUT_MD", "",
              f"Device: {summary.get('device')} ({summary.get('arch')}, {summary.get('cus')} CUs, peak engine clock "
              f"{summary.get('peak_clock_mhz')} MHz as HIP reports it), HIP {summary.get('hip')}; oracle on "
-             f"{summary.get('oracle_threads')} host threads.  Each of forward, backward and forward + backward is "
+             f"{summary.get('oracle_threads')} BLAS threads of {summary.get('host', {}).get('cpu_count')} logical "
+             f"cores ({summary.get('host', {}).get('cpu_model')}).  Each of forward, backward and forward + backward is "
              "timed over 9 runs after one warm-up (HIP events on the launch stream, after ~50 ms of untimed steps); "
              "the table gives the median and, in brackets, the minimum.  TFLOP/s count 14 hd flops per visible "
              "(query, key) pair over the median total; the fraction is of the dense bf16 matrix peak (2500 TFLOP/s) "
