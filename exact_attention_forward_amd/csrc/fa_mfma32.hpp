@@ -39,18 +39,16 @@ __device__ __forceinline__ f32x16 mma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Operand vector of an input storage type, and its element type.
+// Operand vector of an input storage type, and a vector's element type.
 template <typename TIn>
 struct Frag32;
 template <>
 struct Frag32<bf16_t> {
   using V = bf16x8;
-  using E = __bf16;
 };
 template <>
 struct Frag32<f16_t> {
   using V = f16x8;
-  using E = _Float16;
 };
 template <typename V>
 struct VecElem;
