@@ -77,9 +77,12 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
   }
 }
 
-// dQ kernel: one workgroup per (query tile, batch*head).
+// dQ kernel: one workgroup per (query tile, batch*head).  Up to hd 64 the
+// compiler is held to three resident waves per SIMD (at most 168 VGPRs; two
+// values spill at float32 hd 64): 7% faster at float32, B64 H16 T1024 hd64.
 template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int MR, int BC>
-__global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 3 : 1))) void dq_kernel(
+    BwdArgs a) {
   using M = Mma<TIn>;
   using frag = typename M::frag;
   constexpr int NT = NW * 64;
@@ -242,9 +245,12 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
   }
 }
 
-// dK/dV kernel: one workgroup per (key tile, batch*head).
+// dK/dV kernel: one workgroup per (key tile, batch*head).  Up to hd 64 the
+// compiler is held to two resident waves per SIMD (at most 256 VGPRs; left
+// alone it takes 288 and one wave): 20% faster at float32, B64 H16 T1024 hd64.
 template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int MR, int BQ>
-__global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 2 : 1))) void dkv_kernel(
+    BwdArgs a) {
   using M = Mma<TIn>;
   using frag = typename M::frag;
   constexpr int NT = NW * 64;

@@ -54,8 +54,11 @@ struct FwdArgs {
 //                  half-precision P operands any score >= ln 65520 overflows
 //                  (lesson, block "overflow").
 enum Control { kCtlNone = 0, kCtlNoRescale = 1, kCtlNoMax = 2 };
+// Up to hd 64 the compiler is held to three resident waves per SIMD (at most
+// 168 VGPRs, no spills): 11% faster than two at float32, B64 H16 T1024 hd64.
 template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int MR, int BC, int CONTROL = kCtlNone>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 3 : 1))) void fwd_kernel(
+    FwdArgs a) {
   using M = Mma<TIn>;
   using frag = typename M::frag;
   constexpr int NT = NW * 64;

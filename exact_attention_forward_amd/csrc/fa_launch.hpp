@@ -50,7 +50,7 @@ template <int HD>
 struct TileCfg<float, HD> {
   static constexpr int FWD_NW = 4, FWD_MR = 2, FWD_BC = 32;
   static constexpr int DQ_NW = 4, DQ_MR = 2, DQ_BC = 32;
-  static constexpr int DKV_NW = 4, DKV_MR = 2, DKV_BQ = 32;
+  static constexpr int DKV_NW = 4, DKV_MR = HD <= 64 ? 2 : 1, DKV_BQ = 32;  // hd 128: two row tiles spill
 };
 template <>
 struct TileCfg<bf16_t, 64> {
