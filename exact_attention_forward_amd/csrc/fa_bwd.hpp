@@ -245,11 +245,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(HD <= 6
   }
 }
 
-// dK/dV kernel: one workgroup per (key tile, batch*head).  Up to hd 64 the
-// compiler is held to two resident waves per SIMD (at most 256 VGPRs; left
-// alone it takes 288 and one wave): 20% faster at float32, B64 H16 T1024 hd64.
+// dK/dV kernel: one workgroup per (key tile, batch*head).  The compiler is
+// held to two resident waves per SIMD (at most 256 VGPRs; left alone it takes
+// 288 and one wave at float32 hd 64): 20% faster at float32, B64 H16 T1024
+// hd64.
 template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int MR, int BQ>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 2 : 1))) void dkv_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void dkv_kernel(
     BwdArgs a) {
   using M = Mma<TIn>;
   using frag = typename M::frag;

@@ -48,9 +48,10 @@ struct TileCfg32 {
 
 template <int HD>
 struct TileCfg<float, HD> {
-  static constexpr int FWD_NW = 4, FWD_MR = 2, FWD_BC = 32;
-  static constexpr int DQ_NW = 4, DQ_MR = 2, DQ_BC = 32;
-  static constexpr int DKV_NW = 4, DKV_MR = HD <= 64 ? 2 : 1, DKV_BQ = 32;  // hd 128: two row tiles spill
+  static constexpr int FWD_NW = 4, FWD_MR = HD <= 64 ? 2 : 1, FWD_BC = 32;
+  static constexpr int DQ_NW = 4, DQ_MR = HD <= 64 ? 2 : 1, DQ_BC = 32;
+  static constexpr int DKV_NW = 4, DKV_MR = HD <= 64 ? 2 : 1, DKV_BQ = 32;  // hd 128: one row tile per wave fits two
+                                                                            // waves per SIMD without spills
 };
 template <>
 struct TileCfg<bf16_t, 64> {
@@ -141,17 +142,18 @@ int run_dq(const BwdArgs& a, hipStream_t s) {
     const long items = (long)((a.T + C::DQ_NW * 32 - 1) / (C::DQ_NW * 32)) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DQ_NW * 64, items)), dim3(C::DQ_NW * 64), 0, s, a);
     return launch_status();
+  } else {
+    if constexpr (FUSE_D) {  // float32 path: the pre-pass, then the dQ kernel
+      const int st = run_delta<TIn, HD>(a, s);
+      if (st) return st;
+    }
+    using C = TileCfg<TIn, HD>;
+    constexpr int BR = C::DQ_NW * 16 * C::DQ_MR;
+    const long grid = (long)((a.T + BR - 1) / BR) * a.B * a.H;
+    hipLaunchKernelGGL((dq_kernel<TIn, HD, CAUSAL, PREC, C::DQ_NW, C::DQ_MR, C::DQ_BC>), dim3((unsigned)grid),
+                       dim3(C::DQ_NW * 64), 0, s, a);
+    return launch_status();
   }
-  if constexpr (FUSE_D) {  // float32 / half path: the pre-pass, then the dQ kernel
-    const int st = run_delta<TIn, HD>(a, s);
-    if (st) return st;
-  }
-  using C = TileCfg<TIn, HD>;
-  constexpr int BR = C::DQ_NW * 16 * C::DQ_MR;
-  const long grid = (long)((a.T + BR - 1) / BR) * a.B * a.H;
-  hipLaunchKernelGGL((dq_kernel<TIn, HD, CAUSAL, PREC, C::DQ_NW, C::DQ_MR, C::DQ_BC>), dim3((unsigned)grid),
-                     dim3(C::DQ_NW * 64), 0, s, a);
-  return launch_status();
 }
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
@@ -162,13 +164,14 @@ int run_dkv(const BwdArgs& a, hipStream_t s) {
     const long items = (long)((a.T + C::DKV_NW * 32 - 1) / (C::DKV_NW * 32)) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DKV_NW * 64, items)), dim3(C::DKV_NW * 64), 0, s, a);
     return launch_status();
+  } else {
+    using C = TileCfg<TIn, HD>;
+    constexpr int BK = C::DKV_NW * 16 * C::DKV_MR;
+    const long grid = (long)((a.T + BK - 1) / BK) * a.B * a.H;
+    hipLaunchKernelGGL((dkv_kernel<TIn, HD, CAUSAL, PREC, C::DKV_NW, C::DKV_MR, C::DKV_BQ>), dim3((unsigned)grid),
+                       dim3(C::DKV_NW * 64), 0, s, a);
+    return launch_status();
   }
-  using C = TileCfg<TIn, HD>;
-  constexpr int BK = C::DKV_NW * 16 * C::DKV_MR;
-  const long grid = (long)((a.T + BK - 1) / BK) * a.B * a.H;
-  hipLaunchKernelGGL((dkv_kernel<TIn, HD, CAUSAL, PREC, C::DKV_NW, C::DKV_MR, C::DKV_BQ>), dim3((unsigned)grid),
-                     dim3(C::DKV_NW * 64), 0, s, a);
-  return launch_status();
 }
 
 // Split-key forward: partial results of nsplit key ranges into a workspace,
