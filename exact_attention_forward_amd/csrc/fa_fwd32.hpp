@@ -86,9 +86,12 @@ __device__ __forceinline__ int subtile_row(int wave, int u) {
 #ifndef FA_FWD_WPE64
 #define FA_FWD_WPE64 2
 #endif
+#ifndef FA_FWD_WPE128
+#define FA_FWD_WPE128 2
+#endif
 template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int BC, int MS>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(HD <= 64 ? FA_FWD_WPE64 : 1, HD <= 64 ? FA_FWD_WPE64 : 1)))
+__attribute__((amdgpu_waves_per_eu(HD <= 64 ? FA_FWD_WPE64 : FA_FWD_WPE128, HD <= 64 ? FA_FWD_WPE64 : FA_FWD_WPE128)))
 void fwd32_kernel(FwdArgs a) {
   // Persistent: the grid is sized to the resident workgroups and each loops over work items.
   constexpr int NT = NW * 64;

@@ -34,16 +34,28 @@ struct TileCfg;
 #ifndef FA_DKV_BQ64
 #define FA_DKV_BQ64 64
 #endif
+// hd 128: 32-key blocks in the forward and dQ kernels fit two waves per SIMD
+// (forward 217-231 VGPRs, dQ without fused D 232-235); the dK/dV kernel
+// cannot (236 spills at 256) and keeps one.
+#ifndef FA_FWD_BC128
+#define FA_FWD_BC128 32
+#endif
+#ifndef FA_DQ_BC128
+#define FA_DQ_BC128 32
+#endif
+#ifndef FA_DKV_BQ128
+#define FA_DKV_BQ128 64
+#endif
 #ifndef FA_NW64
 #define FA_NW64 4
 #endif
 // FWD_MS: 32-row sub-tiles per wave in the forward (rows per workgroup = 32 NW MS).
 template <int HD>
 struct TileCfg32 {
-  static constexpr int FWD_NW = HD <= 64 ? FA_FWD_NW64 : 4, FWD_BC = HD <= 64 ? FA_FWD_BC64 : 64;
+  static constexpr int FWD_NW = HD <= 64 ? FA_FWD_NW64 : 4, FWD_BC = HD <= 64 ? FA_FWD_BC64 : FA_FWD_BC128;
   static constexpr int FWD_MS = HD <= 64 ? FA_FWD_MS64 : 1;
-  static constexpr int DQ_NW = HD <= 64 ? FA_NW64 : 4, DQ_BC = HD <= 64 ? FA_DQ_BC64 : 64;
-  static constexpr int DKV_NW = HD <= 64 ? FA_NW64 : 4, DKV_BQ = HD <= 64 ? FA_DKV_BQ64 : 64;
+  static constexpr int DQ_NW = HD <= 64 ? FA_NW64 : 4, DQ_BC = HD <= 64 ? FA_DQ_BC64 : FA_DQ_BC128;
+  static constexpr int DKV_NW = HD <= 64 ? FA_NW64 : 4, DKV_BQ = HD <= 64 ? FA_DKV_BQ64 : FA_DKV_BQ128;
 };
 
 template <int HD>
@@ -138,7 +150,13 @@ template <typename TIn, int HD, bool CAUSAL, int PREC, bool FUSE_D = false>
 int run_dq(const BwdArgs& a, hipStream_t s) {
   if constexpr (is_16bit<TIn>) {
     using C = TileCfg32<HD>;
-    auto* k = &dq32_kernel<TIn, HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC, FUSE_D>;
+    // hd 128 takes D from the pre-pass: the O rows for fusing it would need
+    // 64 more VGPRs and the kernel would drop to one wave per SIMD
+    if constexpr (HD > 64 && FUSE_D) {
+      const int st = run_delta<TIn, HD>(a, s);
+      if (st) return st;
+    }
+    auto* k = &dq32_kernel<TIn, HD, CAUSAL, PREC, C::DQ_NW, C::DQ_BC, (HD > 64 ? false : FUSE_D)>;
     const long items = (long)((a.T + C::DQ_NW * 32 - 1) / (C::DQ_NW * 32)) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DQ_NW * 64, items)), dim3(C::DQ_NW * 64), 0, s, a);
     return launch_status();
