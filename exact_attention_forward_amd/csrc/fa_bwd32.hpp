@@ -22,8 +22,8 @@
 #include "fa_mfma32.hpp"
 
 #ifndef FA_DQ_OCC128
-#define FA_DQ_OCC128 2  // two waves per SIMD at hd 128, causal (D from the pre-pass; without the
-                        // mask the kernel would spill)
+#define FA_DQ_OCC128 2  // two waves per SIMD at hd 128 (D from the pre-pass; hd 128 reaches this
+                        // kernel only under the causal mask)
 #endif
 
 namespace fa {
@@ -39,7 +39,7 @@ namespace fa {
 // ones (under the causal mask; without it, right after that block, where
 // fewer values are live), so a new tile starts with its first block in LDS.
 template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int BC, bool FUSE_D>
-__global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : (CAUSAL ? FA_DQ_OCC128 : 1)) void dq32_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : FA_DQ_OCC128) void dq32_kernel(BwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
   constexpr int LD = HD + 8;

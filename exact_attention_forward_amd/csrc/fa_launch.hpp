@@ -148,7 +148,10 @@ int run_delta(const BwdArgs& a, hipStream_t s) {
 
 template <typename TIn, int HD, bool CAUSAL, int PREC, bool FUSE_D = false>
 int run_dq(const BwdArgs& a, hipStream_t s) {
-  if constexpr (is_16bit<TIn>) {
+  // 16-bit hd 128 without the causal mask runs the 16x16 kernel: there the
+  // 32x32 one needs 356-398 VGPRs (one wave per SIMD), and the 16x16 one at
+  // two waves is 13% faster at B4 H16 T8192.
+  if constexpr (is_16bit<TIn> && (HD <= 64 || CAUSAL)) {
     using C = TileCfg32<HD>;
     // hd 128 takes D from the pre-pass: the O rows for fusing it would need
     // 64 more VGPRs and the kernel would drop to one wave per SIMD
