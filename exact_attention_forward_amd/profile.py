@@ -21,6 +21,7 @@ Usage (from the repository root, on the machine where the databases are)::
     python -m exact_attention_forward_amd.profile lab LAB_JSON_LOG FETCH_DB WRITE_DB OUT_MD
     python -m exact_attention_forward_amd.profile configs CONFIGS_LOG OUT_MD
     python -m exact_attention_forward_amd.profile traffic_all FETCH_DB WRITE_DB REQ_DB OUT_MD
+    python -m exact_attention_forward_amd.profile clock GRBM_DB OUT_MD
 
 ``report`` writes the Markdown summaries and ``traffic.json`` of the causal
 B64 H16 T1024 hd64 bfloat16 workload into OUT_DIR; HASH is the kernel source
@@ -425,6 +426,37 @@ def traffic_all_report(fetch_db, write_db, req_db, out_md) -> None:
     Path(out_md).write_text("\n".join(lines) + "\n")
 
 
+XCDS = 8  # MI355X: 256 compute units in 8 accelerator dies, one GRBM_GUI_ACTIVE count each
+
+
+def clock_report(db: str, out_md: str) -> None:
+    """Shader clock each kernel ran at: GRBM_GUI_ACTIVE (summed over the XCDs) / XCDs / dispatch duration."""
+    c = sqlite3.connect(db)
+    rows = c.execute("select dispatch_id, kernel_name, value, duration from counters_collection "
+                     "where counter_name = 'GRBM_GUI_ACTIVE' order by dispatch_id").fetchall()
+    per = collections.defaultdict(list)
+    order = []
+    for _, name, v, dur in rows:
+        k = short_name(name)
+        if k not in per:
+            order.append(k)
+        per[k].append((float(dur), float(v) / XCDS / float(dur)))
+    lines = ["# Shader clock under the attention kernels (MI355X)", "",
+             "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+             "    rocprofv3 --pmc GRBM_GUI_ACTIVE -d gpurun_out/clock -o clock -- python3 bench.py --counters "
+             "--workloads C2,C3,C4",
+             "    python -m exact_attention_forward_amd.profile clock DB OUT_MD", "",
+             f"Clock = GRBM_GUI_ACTIVE summed over the {XCDS} XCDs / {XCDS} / dispatch duration, per dispatch in "
+             "launch order (the first kernels are a fill and the 1 GiB calibration copy).  HIP reports a peak "
+             "engine clock of 2400 MHz.", "",
+             "| kernel | dispatches | mean us | GHz per dispatch |", "|---|---|---|---|"]
+    for k in order:
+        v = per[k]
+        lines.append(f"| `{k}` | {len(v)} | {sum(d for d, _ in v) / len(v) / 1e3:.1f} | "
+                     + ", ".join(f"{g:.2f}" for _, g in v) + " |")
+    Path(out_md).write_text("\n".join(lines) + "\n")
+
+
 def configs_report(log_path, out_md) -> None:
     """Markdown table of a ``bench.py --configs`` log (one JSON line per workload, then a summary line)."""
     recs, summary = [], {}
@@ -468,7 +500,7 @@ def configs_report(log_path, out_md) -> None:
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab", "configs", "traffic_all"))
+    ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab", "configs", "traffic_all", "clock"))
     ap.add_argument("db", nargs="+")
     a = ap.parse_args(argv)
     if a.what == "trace":
@@ -483,6 +515,8 @@ def main(argv=None) -> int:
         configs_report(*a.db[:2])
     elif a.what == "traffic_all":
         traffic_all_report(*a.db[:4])
+    elif a.what == "clock":
+        clock_report(*a.db[:2])
     else:
         report(*a.db[:6])
     return 0
