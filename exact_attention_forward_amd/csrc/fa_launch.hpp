@@ -17,7 +17,7 @@ namespace fa {
 template <typename TIn, int HD>
 struct TileCfg;
 
-// bfloat16 kernels use 32x32 tiles: NW waves of 32 rows each.  The block
+// 16-bit kernels use 32x32 tiles: NW waves of 32 rows each.  The block
 // sizes can be overridden at compile time for tuning sweeps.
 #ifndef FA_FWD_BC64
 #define FA_FWD_BC64 32
@@ -35,8 +35,9 @@ struct TileCfg;
 #define FA_DKV_BQ64 64
 #endif
 // hd 128: 32-key blocks in the forward and dQ kernels fit two waves per SIMD
-// (forward 217-231 VGPRs, dQ without fused D 232-235); the dK/dV kernel
-// cannot (236 spills at 256) and keeps one.
+// (forward 217-231 VGPRs, dQ without fused D 232-235).  The 32x32 dK/dV
+// kernel cannot (236 spills at 256), so 16-bit hd 128 dK/dV, and dQ without
+// the causal mask, run the 16x16 kernels (see run_dq, run_dkv).
 #ifndef FA_FWD_BC128
 #define FA_FWD_BC128 32
 #endif
@@ -50,6 +51,7 @@ struct TileCfg;
 #define FA_NW64 4
 #endif
 // FWD_MS: 32-row sub-tiles per wave in the forward (rows per workgroup = 32 NW MS).
+// (DKV_BQ at hd 128 only matters to the 32x32 kernel, which hd 128 no longer uses.)
 template <int HD>
 struct TileCfg32 {
   static constexpr int FWD_NW = HD <= 64 ? FA_FWD_NW64 : 4, FWD_BC = HD <= 64 ? FA_FWD_BC64 : FA_FWD_BC128;
