@@ -1,6 +1,7 @@
 // Kernel instantiation and launch helpers shared by the per-dtype translation
 // units.  Tile shapes per (input type, head dim) live in TileCfg.
 #pragma once
+#include <atomic>
 #include <type_traits>
 
 #include "fa_bwd.hpp"
@@ -84,28 +85,30 @@ struct TileCfg<bf16_t, 128> {
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? 0 : -5; }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; calls from
+// several host threads may fill an entry concurrently with the same value).
 inline int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 // Grid for a persistent kernel: every resident workgroup slot, at most one per item.
 template <typename K>
 inline long persistent_grid(K kernel, int threads, long items) {
-  static int per_cu = 0;  // one value per kernel instantiation
-  if (per_cu == 0) {
+  // resident workgroups per compute unit, one value per kernel instantiation
+  // (a function-local static is initialised once, also under concurrent calls)
+  static const int per_cu = [&] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
-    per_cu = n;
-  }
+    return n;
+  }();
   const long slots = (long)per_cu * device_cus();
   return items < slots ? items : slots;
 }
