@@ -35,11 +35,13 @@ struct FwdArgs {
   int B, H, T;
   float c2;                    // scale * log2(e)
   unsigned one2 = 0x3F803F80u;  // bfloat16 pair (1, 1): a scalar operand for row sums by dot products
-  // Key split (fwd_kernel only): blockIdx.y = s handles keys [s kchunk,
-  // (s + 1) kchunk) and writes its partial O and L at o + s o_split,
-  // lse + s lse_split.  kchunk = 0: one split covering every key.
+  // Key split: split s handles keys [s kchunk, (s + 1) kchunk) and writes its
+  // partial O and L at o + s o_split, lse + s lse_split (fwd_kernel: split =
+  // blockIdx.y; fwd32_kernel: nsplit splits per query tile among its work
+  // items).  kchunk = 0: one split covering every key.
   int kchunk = 0;
   size_t o_split = 0, lse_split = 0;
+  int nsplit = 1;
 };
 
 // PREC: 0 = operands rounded to bfloat16 (or exact f32), 1 = P split into a

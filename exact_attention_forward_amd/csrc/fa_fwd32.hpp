@@ -89,7 +89,10 @@ __device__ __forceinline__ int subtile_row(int wave, int u) {
 #ifndef FA_FWD_WPE128
 #define FA_FWD_WPE128 2
 #endif
-template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int BC, int MS>
+// SPLIT: the work items are (query tile, head, key split) and each writes a
+// partial O and L for the merge; false compiles the plain kernel with the
+// split bookkeeping folded away.
+template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int BC, int MS, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(HD <= 64 ? FA_FWD_WPE64 : FA_FWD_WPE128, HD <= 64 ? FA_FWD_WPE64 : FA_FWD_WPE128)))
 void fwd32_kernel(FwdArgs a) {
@@ -121,12 +124,15 @@ void fwd32_kernel(FwdArgs a) {
   for (int p = 0; p < Copy::PER; ++p) goff[p] = (unsigned)((Copy::vrow(tid, p) * rs + Copy::vcol(tid, p)) * 2);
 
   const int nqt = (T + BR - 1) / BR;
-  const int total = nqt * a.B * H;
+  const int nsp = SPLIT ? a.nsplit : 1;  // key splits per query tile
+  const int total = nqt * a.B * H * nsp;
   for (int round = 0;; ++round) {
     const int w = persistent_item(round, total);
     if (w < 0) break;
-    const int bh = w / nqt;
-    const int qt = nqt - 1 - (w % nqt);
+    const int sp = SPLIT ? w % nsp : 0;
+    const int wq = SPLIT ? w / nsp : w;
+    const int bh = wq / nqt;
+    const int qt = nqt - 1 - (wq % nqt);
     const int b = bh / H, hh = bh % H;
     const size_t base = ((size_t)b * T * H + hh) * HD;
     const bf16_t* Q = static_cast<const bf16_t*>(a.q) + base;
@@ -134,6 +140,12 @@ void fwd32_kernel(FwdArgs a) {
     const bf16_t* V = static_cast<const bf16_t*>(a.v) + base;
     const int i0 = qt * BR;
     const int nkb = CAUSAL ? ((min(i0 + BR, T) - 1) / BC + 1) : (T + BC - 1) / BC;
+    // this split's key blocks (none when its range starts past the visible keys:
+    // then O = 0 and L = -inf, which the merge skips)
+    const int kb_lo = SPLIT ? sp * (a.kchunk / BC) : 0;
+    const int kb_end = SPLIT ? min(nkb, kb_lo + a.kchunk / BC) : nkb;
+    float* const Og = SPLIT ? a.o + (size_t)sp * a.o_split : a.o;
+    float* const Lg = SPLIT ? a.lse + (size_t)sp * a.lse_split : a.lse;
 
     V8 qf[MS][NKS];
     f32x16 oacc[MS][NDT];
@@ -166,10 +178,12 @@ void fwd32_kernel(FwdArgs a) {
         cv.load_clamped(V, rs, j, T, tid);
       }
     };
-    fetch(0);
-    ck.store(sK[0], LD, tid);
-    cv.store(sV[0], LD, tid);
-    __syncthreads();
+    if (!SPLIT || kb_lo < kb_end) {  // uniform over the workgroup
+      fetch(kb_lo * BC);
+      ck.store(sK[0], LD, tid);
+      cv.store(sV[0], LD, tid);
+      __syncthreads();
+    }
 
     // Mask and reference-max update (with rescale) for one sub-tile's raw
     // scores s of the block at key j0.
@@ -269,10 +283,10 @@ void fwd32_kernel(FwdArgs a) {
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
 
-    for (int kb = 0; kb < nkb; ++kb) {
+    for (int kb = kb_lo; kb < kb_end; ++kb) {
       const int j0 = kb * BC;
-      const int buf = kb & 1;
-      if (kb + 1 < nkb) fetch(j0 + BC);
+      const int buf = (kb - kb_lo) & 1;
+      if (kb + 1 < kb_end) fetch(j0 + BC);
       int code = 0;
 #pragma unroll
       for (int u = 0; u < MS; ++u) {
@@ -297,7 +311,7 @@ void fwd32_kernel(FwdArgs a) {
         if (code == 1) block(cK, cV, j0, I1{}, I0{});
         else if (code == 2) block(cK, cV, j0, I2{}, I0{});
       }
-      if (kb + 1 < nkb) {
+      if (kb + 1 < kb_end) {
         ck.store(sK[buf ^ 1], LD, tid);
         cv.store(sV[buf ^ 1], LD, tid);
       }
@@ -309,7 +323,7 @@ void fwd32_kernel(FwdArgs a) {
       const int row = r0[u] + n;
       const float l = half_swap_sum(ls0[u] + ls1[u]);
       if (row < T) {
-        float* O = a.o + base + (size_t)row * rs;
+        float* O = Og + base + (size_t)row * rs;
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -319,7 +333,7 @@ void fwd32_kernel(FwdArgs a) {
                         oacc[u][dt][4 * bb + 3] * inv};
             *reinterpret_cast<f32x4*>(O + 32 * dt + 8 * bb + 4 * h) = v4;
           }
-        if (h == 0) a.lse[(size_t)bh * T + row] = l > 0.f ? (mref[u] + log2f(l)) * kLn2 : -INFINITY;
+        if (h == 0) Lg[(size_t)bh * T + row] = l > 0.f ? (mref[u] + log2f(l)) * kLn2 : -INFINITY;
       }
     }
   }

@@ -214,17 +214,28 @@ struct SplitArgs {
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_fwd_split(const SplitArgs& sa, hipStream_t s) {
-  using C = TileCfg<TIn, HD>;
-  constexpr int BR = C::FWD_NW * 16 * C::FWD_MR;
   FwdArgs a = sa.f;
   const size_t n = (size_t)a.B * a.T * a.H * HD, nr = (size_t)a.B * a.H * a.T;
   const int per = (a.T + sa.nsplit - 1) / sa.nsplit;
-  a.kchunk = (per + C::FWD_BC - 1) / C::FWD_BC * C::FWD_BC;
   a.o_split = n;
   a.lse_split = nr;
-  const long nqt = (a.T + BR - 1) / BR;
-  hipLaunchKernelGGL((fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC>),
-                     dim3((unsigned)(nqt * a.B * a.H), (unsigned)sa.nsplit), dim3(C::FWD_NW * 64), 0, s, a);
+  a.nsplit = sa.nsplit;
+  if constexpr (is_16bit<TIn>) {  // the 32x32 forward, (query tile, head, split) work items
+    using C = TileCfg32<HD>;
+    a.kchunk = (per + C::FWD_BC - 1) / C::FWD_BC * C::FWD_BC;
+    if constexpr (!is_bf16<TIn>) a.one2 = 0x3C003C00u;
+    auto* k = &fwd32_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC, C::FWD_MS, true>;
+    constexpr int BR = C::FWD_NW * 32 * C::FWD_MS;
+    const long items = (long)((a.T + BR - 1) / BR) * a.B * a.H * sa.nsplit;
+    hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::FWD_NW * 64, items)), dim3(C::FWD_NW * 64), 0, s, a);
+  } else {
+    using C = TileCfg<TIn, HD>;
+    constexpr int BR = C::FWD_NW * 16 * C::FWD_MR;
+    a.kchunk = (per + C::FWD_BC - 1) / C::FWD_BC * C::FWD_BC;
+    const long nqt = (a.T + BR - 1) / BR;
+    hipLaunchKernelGGL((fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC>),
+                       dim3((unsigned)(nqt * a.B * a.H), (unsigned)sa.nsplit), dim3(C::FWD_NW * 64), 0, s, a);
+  }
   if (launch_status()) return -5;
   MergeArgs m{a.o, a.lse, sa.o, sa.lse, a.B, a.H, a.T, sa.nsplit, n, nr};
   constexpr int RPB = 256 / (HD / 4);

@@ -85,7 +85,8 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
  * the fused-attention lesson, block "sources.onlineSoftmax", claim that the
  * merge is associative and commutative).  More workgroups per query tile:
  * for few (batch, head) pairs and long T.  Results equal fa_forward's up to
- * float32 rounding order (not bit for bit).
+ * rounding (not bit for bit): float32 summation order, and for 16-bit inputs
+ * the rounding of P, which each split takes against its own running max.
  *   ws      float32 workspace of nsplit * (B*T*H*hd + B*H*T) elements,
  *           caller-allocated; overwritten
  *   nsplit  1 .. 64

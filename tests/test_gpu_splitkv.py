@@ -55,14 +55,17 @@ def test_splitkv_f32(shape, causal, nsplit):
     assert err["O"] <= F32_TOL and err["L"] <= F32_TOL, err
 
 
-@pytest.mark.parametrize("nsplit", [1, 4, 13])
+@pytest.mark.parametrize("prec", [fa.FA_PREC_BF16, fa.FA_PREC_DEFAULT])
+@pytest.mark.parametrize("nsplit", [1, 4, 13, 64])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("hd", [64, 128])
-def test_splitkv_bf16(hd, causal, nsplit):
+def test_splitkv_bf16(hd, causal, nsplit, prec):
+    # 64 splits of T = 777 round to 32-key chunks: 25 hold keys, the rest are
+    # empty and must come out as O = 0, L = -inf partials that the merge skips.
     c = I.make_case("split_bf16", 1, 2, 777, hd, I.BF16, causal, 400 + hd)
-    o, lse = run_split(c, nsplit, fa.FA_PREC_BF16)
+    o, lse = run_split(c, nsplit, prec)
     err = oracle_errors(c, o, lse)
-    print(f"[split] bf16 hd={hd} causal={causal} nsplit={nsplit} {err}", flush=True)
+    print(f"[split] bf16 hd={hd} causal={causal} nsplit={nsplit} prec={prec} {err}", flush=True)
     assert err["O"] <= BF16_TOL and err["L"] <= BF16_TOL, err
 
 
