@@ -165,9 +165,9 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
     fr = fused_requests(T, hd, fwd_rows, True)
     fr_nc = fused_requests(T, hd, fwd_rows, False)
     lines = [f"# HBM traffic per launch: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
-             "Commands (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, paths absolute):",
-             "", "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch -- python3 bench.py --counters",
-             "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write -- python3 bench.py --counters",
+             "Commands (from the repository root on an MI355X, after `cd /tmp && export TMPDIR=/tmp`, paths absolute, $OUT a scratch directory):",
+             "", "    rocprofv3 --pmc FETCH_SIZE -d $OUT/prof_fetch -o fetch -- python3 bench.py --counters",
+             "    rocprofv3 --pmc WRITE_SIZE -d $OUT/prof_write -o write -- python3 bench.py --counters",
              "    python -m exact_attention_forward_amd.profile report ...", "",
              f"Calibration: the same counters on a plain device copy of 1 GiB (`{COPY_KERNEL}`) read FETCH_SIZE "
              f"{tr['copy_fetch_kib']:.1f} KiB and WRITE_SIZE {tr['copy_write_kib']:.1f} KiB for 1048576 KiB moved each "
@@ -198,17 +198,17 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
     (out / f"hbm_traffic_gpt2m_bf16.md").write_text("\n".join(lines) + "\n")
 
     lines = [f"# Kernel trace: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
-             "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, paths absolute):",
-             "", "    rocprofv3 --kernel-trace --stats -d gpurun_out/prof_trace -o trace -- "
+             "Command (from the repository root on an MI355X, after `cd /tmp && export TMPDIR=/tmp`, paths absolute, $OUT a scratch directory):",
+             "", "    rocprofv3 --kernel-trace --stats -d $OUT/prof_trace -o trace -- "
              "python3 bench.py --no-cpu-baseline --steps 20", "", trace_table(trace_db)]
     (out / "kernel_trace_gpt2m_bf16.md").write_text("\n".join(lines) + "\n")
 
     flops = {"fwd32_kernel": 4, "dq32_kernel": 6, "dkv32_kernel": 8}
     pairs = heads * T * T / 2
     lines = [f"# Matrix-core and vector-ALU use: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
-             "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, paths absolute):", "",
+             "Command (from the repository root on an MI355X, after `cd /tmp && export TMPDIR=/tmp`, paths absolute, $OUT a scratch directory):", "",
              "    rocprofv3 --pmc MfmaUtil VALUBusy LDSBankConflict OccupancyPercent SQ_INSTS_VALU_MFMA_MOPS_BF16 "
-             "-d gpurun_out/prof_util -o util -- python3 bench.py --counters", "",
+             "-d $OUT/prof_util -o util -- python3 bench.py --counters", "",
              "MfmaUtil = busy cycles of the matrix cores over (GPU-active cycles x SIMDs); executed bf16 matrix flops = "
              "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; algorithmic flops count hd-long products per visible (query, key) pair "
              "(forward 4 hd, dQ kernel 6 hd, dK/dV kernel 8 hd; B H T^2 / 2 pairs).", "",
@@ -273,11 +273,11 @@ def lab_report(lab_log: str, fetch_db: str, write_db: str, out_md: str) -> None:
             rec = json.loads(line)
     by = lab_bytes(fetch_db, write_db)
     lines = ["# Lab of the fused-attention lesson on MI355X: fused vs unfused forward, one head, no mask, float32", "",
-             "Commands (from the repository root on the GPU box; the rocprofv3 runs after `cd /tmp && export "
-             "TMPDIR=/tmp`, paths absolute):", "",
+             "Commands (from the repository root on an MI355X; the rocprofv3 runs after `cd /tmp && export "
+             "TMPDIR=/tmp`, paths absolute, $OUT a scratch directory):", "",
              "    python bench.py --lab",
-             "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/lab_fetch -o fetch -- python3 bench.py --lab --counters",
-             "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/lab_write -o write -- python3 bench.py --lab --counters",
+             "    rocprofv3 --pmc FETCH_SIZE -d $OUT/lab_fetch -o fetch -- python3 bench.py --lab --counters",
+             "    rocprofv3 --pmc WRITE_SIZE -d $OUT/lab_write -o write -- python3 bench.py --lab --counters",
              "    python -m exact_attention_forward_amd.profile lab ...", "",
              "Inputs: q, k, v uniform in [-2, 2), seed 1, scale 1/sqrt(d).  Times: median of 9 runs after one warm-up "
              "(HIP events; the unfused forward's three kernels in one timed run).  Bytes: FETCH_SIZE and WRITE_SIZE "
@@ -399,13 +399,13 @@ def traffic_all_report(fetch_db, write_db, req_db, out_md) -> None:
         tr = mean(r.get(k, {}).get("SQ_INSTS_VALU_TRANS_F32", [])) * 64
         rows.append((wl, short_name(k), m, hr, hw, lr, lw, tr))
     lines = ["# L2 requests and HBM bytes of every kernel against its tile walk (MI355X)", "",
-             "Commands (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
-             "    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/all_fetch -o f -- python3 bench.py --counters "
+             "Commands (from the repository root on an MI355X, after `cd /tmp && export TMPDIR=/tmp`; $OUT is a scratch directory):", "",
+             "    rocprofv3 --pmc FETCH_SIZE -d $OUT/all_fetch -o f -- python3 bench.py --counters "
              "--workloads C2,C3,C4",
-             "    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/all_write -o w -- python3 bench.py --counters "
+             "    rocprofv3 --pmc WRITE_SIZE -d $OUT/all_write -o w -- python3 bench.py --counters "
              "--workloads C2,C3,C4",
              "    rocprofv3 --pmc TCP_TCC_READ_REQ_sum TCP_TCC_WRITE_REQ_sum SQ_INSTS_VALU_TRANS_F32 "
-             "-d gpurun_out/all_req -o r -- python3 bench.py --counters --workloads C2,C3,C4",
+             "-d $OUT/all_req -o r -- python3 bench.py --counters --workloads C2,C3,C4",
              "    python -m exact_attention_forward_amd.profile traffic_all F_DB W_DB R_DB OUT_MD", "",
              f"Calibration on a 1 GiB device copy: HBM reads x{rs:.4f}, writes x{ws:.4f}; one L1-to-L2 read "
              f"request = {l2r:.1f} B, one write request = {l2w:.1f} B.  Requested = the bytes the kernel's tile "
@@ -442,8 +442,8 @@ def clock_report(db: str, out_md: str) -> None:
             order.append(k)
         per[k].append((float(dur), float(v) / XCDS / float(dur)))
     lines = ["# Shader clock under the attention kernels (MI355X)", "",
-             "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
-             "    rocprofv3 --pmc GRBM_GUI_ACTIVE -d gpurun_out/clock -o clock -- python3 bench.py --counters "
+             "Command (from the repository root on an MI355X, after `cd /tmp && export TMPDIR=/tmp`; $OUT is a scratch directory):", "",
+             "    rocprofv3 --pmc GRBM_GUI_ACTIVE -d $OUT/clock -o clock -- python3 bench.py --counters "
              "--workloads C2,C3,C4",
              "    python -m exact_attention_forward_amd.profile clock DB OUT_MD", "",
              f"Clock = GRBM_GUI_ACTIVE summed over the {XCDS} XCDs / {XCDS} / dispatch duration, per dispatch in "
@@ -466,9 +466,9 @@ def configs_report(log_path, out_md) -> None:
         elif line.startswith('{"configs"'):
             summary = json.loads(line)
     lines = ["# Every workload: parity, forward / backward times and the oracle's time (MI355X)", "",
-             "Command (from the repository root on the GPU box):", "",
-             "    python bench.py --configs > gpurun_out/configs.log",
-             "    python -m exact_attention_forward_amd.profile configs gpurun_out/configs.log OUT_MD", "",
+             "Command (from the repository root on an MI355X; $OUT is a scratch directory):", "",
+             "    python bench.py --configs > $OUT/configs.log",
+             "    python -m exact_attention_forward_amd.profile configs $OUT/configs.log OUT_MD", "",
              f"Device: {summary.get('device')} ({summary.get('arch')}, {summary.get('cus')} CUs, peak engine clock "
              f"{summary.get('peak_clock_mhz')} MHz as HIP reports it), HIP {summary.get('hip')}; oracle on "
              f"{summary.get('oracle_threads')} BLAS threads of {summary.get('host', {}).get('cpu_count')} logical "
