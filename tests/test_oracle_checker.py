@@ -5,7 +5,7 @@ prints for its checker (block ``controls.checker``: N 256, d 16, tiles of 16):
 the tiled float32 output passes, the exact answer rounded to float32 passes,
 one output moved by 0.001 fails with exactly one mismatch, and zero tolerance
 rejects the float32 output.  The inputs follow the page's correctness recipe
-(uniform in [-2, 2), seed 1, scale 1/sqrt(d)) with this build's generator, so
+(uniform in [-2, 2), seed 1, scale 1/sqrt(d)) with NumPy's PCG64 generator, so
 mismatch counts of the broken variant are not compared with the page's
 (parity unpinned: they depend on the page's generator).
 """
