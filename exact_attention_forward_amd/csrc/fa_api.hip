@@ -53,6 +53,10 @@ int check_common(int B, int H, int T, int hd, int dtype, int prec) {
   const double elems = (double)B * H * T * hd;
   if (elems >= 1099511627776.0) return FA_ERR_ARG;  // 2^40
   if ((double)B * H * T >= 2147483647.0) return FA_ERR_ARG;
+  // the 32x32 forward keeps each thread's offsets within a 32-row key block
+  // as 32-bit byte offsets: 32 rows of H * hd 16-bit elements must stay
+  // under 4 GiB
+  if ((double)H * hd >= 33554432.0) return FA_ERR_ARG;  // 2^25
   if (!supported(hd, dtype)) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_BF16 && prec != FA_PREC_DEFAULT) return FA_ERR_UNSUPPORTED;
   return FA_OK;

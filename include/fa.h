@@ -29,7 +29,10 @@
  *           checks happen before the first launch, so a failing call writes
  *           nothing.  A launch failure reports FA_ERR_LAUNCH; kernels already
  *           enqueued by that call may have run.
- * Sizes.    B, H, T >= 1; B * H * T * hd < 2^40 elements.
+ * Sizes.    B, H, T >= 1; B * H * T < 2^31 rows; B * H * T * hd < 2^40
+ *           elements; H * hd < 2^25 (the row stride, in elements: the 16-bit
+ *           forward addresses the rows of a key block with 32-bit byte
+ *           offsets).  Larger sizes return FA_ERR_ARG.
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H

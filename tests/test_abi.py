@@ -88,6 +88,7 @@ def bwd(**kw):
     (dict(dtype=5), fa.FA_ERR_ARG),
     (dict(prec=9), fa.FA_ERR_ARG),
     (dict(B=1 << 20, H=1 << 11, T=1 << 11), fa.FA_ERR_ARG),
+    (dict(H=1 << 19, T=32, dtype=fa.FA_BF16), fa.FA_ERR_ARG),  # H * hd = 2^25: row stride over the limit
     (dict(hd=96), fa.FA_ERR_UNSUPPORTED),
     (dict(hd=32, dtype=fa.FA_BF16), fa.FA_ERR_UNSUPPORTED),
     (dict(prec=fa.FA_PREC_BF16X2), fa.FA_ERR_UNSUPPORTED),
