@@ -42,6 +42,15 @@ with the median milliseconds and the unfused/fused ratio.  Parity of these
 kernels against the float64 reference with the lesson's error bound is checked
 by tests/test_gpu_lab.py.  ``--lab --counters`` instead runs the calibration
 copy and then each (N, d, kind) once, for rocprofv3 --pmc.
+
+``--split`` times the split-key forward against the plain forward on causal
+workloads with few (batch, head) pairs and long sequences (B1 H4 T8192 hd128,
+B1 H8 T16384 hd64, B1 H2 T32768 hd128 in bfloat16, B1 H4 T8192 hd64 in
+float32; seeded N(0, 1) inputs): the plain forward and 2, 4, 8, 16 and 32
+splits, each the median of 9 runs after one warm-up (merge included), with the
+largest difference of O and L between the split and the plain results.  Parity
+of the split forward against the oracle is checked by tests/test_gpu_splitkv.py
+and tests/test_gpu_fp16.py.
 """
 from __future__ import annotations
 
@@ -122,6 +131,8 @@ def parse():
                     help="with --counters: comma-separated workloads to step (C2 f32, C3 bf16, C4 long bf16)")
     ap.add_argument("--lab", action="store_true", help="fused vs unfused lab of the lesson (one head, float32)")
     ap.add_argument("--configs", action="store_true", help="time and check every workload, not only the bench one")
+    ap.add_argument("--split", action="store_true",
+                    help="split-key forward against the plain forward on few-head long-sequence workloads")
     return ap.parse_args()
 
 
@@ -142,6 +153,8 @@ def main() -> int:
         return lab(args)
     if args.configs:
         return configs(args)
+    if args.split:
+        return split(args)
 
     case = I.gpt2m_case(I.BF16)
     B, H, T, hd = case.B, case.H, case.T, case.hd
@@ -300,6 +313,83 @@ def lab(args) -> int:
 
 PEAK_F32_MATRIX_TFLOPS = 157.3  # MI355X dense float32 MFMA
 
+# Few (batch, head) pairs and long sequences, causal: one workgroup per query
+# tile leaves most of the 256 CUs idle, which the key split is for.
+# (B, H, T, hd, dtype, seed)
+SPLIT_WORKLOADS = ((1, 4, 8192, 128, "bf16", 21), (1, 8, 16384, 64, "bf16", 22), (1, 2, 32768, 128, "bf16", 23),
+                   (1, 4, 8192, 64, "f32", 24))
+SPLIT_COUNTS = (2, 4, 8, 16, 32)
+
+
+def split(args) -> int:
+    """Split-key forward against the plain forward: median times and the largest
+    differences of O and L between the two (the merge is exact up to rounding)."""
+    import numpy as np
+    import torch
+
+    import exact_attention_forward_amd as fa
+    from exact_attention_forward_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def median_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(9):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[4]
+
+    rows = []
+    for B, H, T, hd, dts, seed in SPLIT_WORKLOADS:
+        dtype = {"bf16": I.BF16, "f32": I.F32}[dts]
+        case = I.make_case(f"split_B{B}H{H}T{T}hd{hd}_{dts}", B, H, T, hd, dtype, True, seed)
+        if dtype == I.BF16:
+            up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        q, k, v = (up(getattr(case, n)) for n in ("q", "k", "v"))
+        dt = fa.FA_BF16 if dtype == I.BF16 else fa.FA_F32
+        prec = fa.FA_PREC_BF16 if dtype == I.BF16 else fa.FA_PREC_DEFAULT
+        o = torch.empty((B, T, H, hd), device=dev)
+        lse = torch.empty((B, H, T), device=dev)
+        n, nr = B * T * H * hd, B * H * T
+        plain = lambda: fa.check(fa.fa_forward(q, k, v, o, lse, B, H, T, hd, case.scale, 1, dt, prec, stream))
+        t_end = time.perf_counter() + 0.05  # settle the clock
+        while time.perf_counter() < t_end:
+            plain()
+            torch.cuda.synchronize()
+        t_plain = median_ms(plain)
+        o_ref, l_ref = o.clone(), lse.clone()
+        flops = 4 * hd * B * H * T * T / 2
+        row = {"workload": case.name, "B": B, "H": H, "T": T, "hd": hd, "dtype": dts, "causal": True,
+               "precision": int(prec), "plain_ms": round(t_plain, 5),
+               "plain_tflops": round(flops / (t_plain * 1e-3) / 1e12, 2), "splits": []}
+        ws = torch.empty((max(SPLIT_COUNTS) * (n + nr),), device=dev)
+        for ns in SPLIT_COUNTS:
+            o.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            fn = lambda: fa.check(fa.fa_forward_splitkv(q, k, v, o, lse, ws, B, H, T, hd, case.scale, 1, ns, dt,
+                                                        prec, stream))
+            t = median_ms(fn)
+            row["splits"].append({"nsplit": ns, "ms": round(t, 5), "speedup": round(t_plain / t, 3),
+                                  "tflops": round(flops / (t * 1e-3) / 1e12, 2),
+                                  "max_abs_diff_O": float(f"{float((o - o_ref).abs().max()):.3e}"),
+                                  "max_abs_diff_L": float(f"{float((lse - l_ref).abs().max()):.3e}")})
+        print(json.dumps(row), flush=True)
+        rows.append(row)
+        del q, k, v, o, lse, ws, o_ref, l_ref, case
+        torch.cuda.empty_cache()
+    print(json.dumps({"split_workloads": len(rows), "reps": 9, "warmup": 1,
+                      "statistic": "median ms (HIP events, merge included)", **device_label(dev)}), flush=True)
+    return 0
+
 
 def counter_steps(name: str, steps: int = 2) -> None:
     """A few forward + backward steps of workload C2 (float32) or C4 (long context) for a counter run."""
@@ -377,7 +467,6 @@ def configs(args) -> int:
     import exact_attention_forward_amd as fa
     from exact_attention_forward_amd import api
     from exact_attention_forward_amd import inputs as I
-    from oracle import attention as oracle
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -404,17 +493,7 @@ def configs(args) -> int:
         heads = [(b, h) for b in range(B) for h in range(H)]
         if len(heads) > 4:
             heads = [heads[0], heads[len(heads) // 3], heads[2 * len(heads) // 3], heads[-1]]
-        worst, t_oracle = {}, None
-        for b, h in heads:
-            qh, kh, vh, dh = (case.head_f64(n, b, h) for n in ("q", "k", "v", "do"))
-            t0 = time.perf_counter()
-            O, L, _ = oracle.head_forward(qh, kh, vh, case.scale, case.causal)
-            dQ, dK, dV, _ = oracle.head_backward(qh, kh, vh, dh, case.scale, case.causal)
-            if t_oracle is None:
-                t_oracle = time.perf_counter() - t0
-            for n, got, ref in (("O", o[b, :, h], O), ("L", lse[b, h], L), ("dQ", dq[b, :, h], dQ),
-                                ("dK", dk[b, :, h], dK), ("dV", dv[b, :, h], dV)):
-                worst[n] = max(worst.get(n, 0.0), float(np.abs(got.cpu().numpy().astype(np.float64) - ref).max()))
+        worst, t_oracle = cpu_baseline_heads(case, dict(O=o, L=lse, dQ=dq, dK=dk, dV=dv), heads)
         tol = 2e-5 if case.dtype == I.F32 else 2e-2
         ok = all(e <= tol for e in worst.values())
         dt = {I.F32: fa.FA_F32, I.BF16: fa.FA_BF16, I.F16: fa.FA_F16}[case.dtype]
@@ -467,6 +546,27 @@ def configs(args) -> int:
                       "reps": 9, "warmup": 1, "statistic": "median and min ms (HIP events)",
                       "oracle_threads": host_label()["blas_threads"], "host": host_label(), **label}), flush=True)
     return 0 if all(r["parity"]["ok"] for r in summary) else 1
+
+
+def cpu_baseline_heads(case, out, heads):
+    """The oracle on the given heads: worst error of each output against it, and the
+    oracle's time for the first head (the CPU baseline of one workload)."""
+    import numpy as np
+
+    from oracle import attention as oracle
+
+    worst, t_first = {}, None
+    for b, h in heads:
+        qh, kh, vh, dh = (case.head_f64(n, b, h) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        O, L, _ = oracle.head_forward(qh, kh, vh, case.scale, case.causal)
+        dQ, dK, dV, _ = oracle.head_backward(qh, kh, vh, dh, case.scale, case.causal)
+        if t_first is None:
+            t_first = time.perf_counter() - t0
+        for n, ref in (("O", O), ("L", L), ("dQ", dQ), ("dK", dK), ("dV", dV)):
+            g = out[n][b, h] if n == "L" else out[n][b, :, h]
+            worst[n] = max(worst.get(n, 0.0), float(np.abs(g.cpu().numpy().astype(np.float64) - ref).max()))
+    return worst, t_first
 
 
 def cpu_baseline(case, out, budget_s: float):

@@ -498,9 +498,45 @@ def configs_report(log_path, out_md) -> None:
     Path(out_md).write_text("\n".join(lines) + "\n")
 
 
+def split_report(log_path, out_md) -> None:
+    """Markdown table of a ``bench.py --split`` log (one JSON line per workload, then a summary line)."""
+    recs, summary = [], {}
+    for line in Path(log_path).read_text().splitlines():
+        if line.startswith('{"workload"'):
+            recs.append(json.loads(line))
+        elif line.startswith('{"split_workloads"'):
+            summary = json.loads(line)
+    counts = [s["nsplit"] for s in recs[0]["splits"]] if recs else []
+    lines = ["# Split-key forward against the plain forward, few heads and long sequences (MI355X)", "",
+             "Command (from the repository root on an MI355X; $OUT is a scratch directory):", "",
+             "    python bench.py --split > $OUT/split.log",
+             "    python -m exact_attention_forward_amd.profile split $OUT/split.log OUT_MD", "",
+             f"Device: {summary.get('device')} ({summary.get('arch')}, {summary.get('cus')} CUs), HIP "
+             f"{summary.get('hip')}.  Causal workloads with few (batch, head) pairs, seeded N(0, 1) inputs; "
+             "bfloat16 at the bf16-operand precision, float32 at its default.  Each entry is the median of 9 runs "
+             "after one warm-up (HIP events on the launch stream; the split runs include the merge kernel), in "
+             "ms, with the speed-up over the plain forward in brackets.  TFLOP/s count 4 hd flops per visible "
+             "(query, key) pair.  The last columns give the largest |O_split - O_plain| and |L_split - L_plain| "
+             "over every split count (the merge is exact up to rounding; for 16-bit inputs each split also rounds "
+             "P against its own running max).", "",
+             "| workload | plain ms (TFLOP/s) | " + " | ".join(f"{c} splits" for c in counts) +
+             " | best split (TFLOP/s) | max diff O | max diff L |",
+             "|---|---|" + "---|" * len(counts) + "---|---|---|"]
+    for r in recs:
+        best = max(r["splits"], key=lambda x: x["speedup"])
+        cells = " | ".join(f"{x['ms']:.4f} ({x['speedup']:.2f}x)" for x in r["splits"])
+        dO = max(x["max_abs_diff_O"] for x in r["splits"])
+        dL = max(x["max_abs_diff_L"] for x in r["splits"])
+        lines.append(f"| B{r['B']} H{r['H']} T{r['T']} hd{r['hd']} {r['dtype']} | {r['plain_ms']:.4f} "
+                     f"({r['plain_tflops']:.1f}) | {cells} | {best['tflops']:.1f} ({best['nsplit']} splits) | "
+                     f"{dO:.2e} | {dL:.2e} |")
+    Path(out_md).write_text("\n".join(lines) + "\n")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab", "configs", "traffic_all", "clock"))
+    ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab", "configs", "traffic_all", "clock",
+                                     "split"))
     ap.add_argument("db", nargs="+")
     a = ap.parse_args(argv)
     if a.what == "trace":
@@ -517,6 +553,8 @@ def main(argv=None) -> int:
         traffic_all_report(*a.db[:4])
     elif a.what == "clock":
         clock_report(*a.db[:2])
+    elif a.what == "split":
+        split_report(*a.db[:2])
     else:
         report(*a.db[:6])
     return 0

@@ -47,3 +47,27 @@ def test_kernel_names_map_to_workloads():
     assert P.workload_of("void fa::dq_kernel<float, 64, true, 0, 4, 2, 32, false>(fa::BwdArgs)") == "C2"
     assert P.workload_of("__amd_rocclr_copyBuffer") is None
     assert P.family("void fa::delta_kernel<float, 64>(fa::BwdArgs)") == "delta_kernel"
+
+
+def test_split_report_table(tmp_path):
+    """The split summary has one row per workload, one column per split count, and picks the fastest split."""
+    import json
+
+    from exact_attention_forward_amd import profile
+
+    row = {"workload": "w", "B": 1, "H": 4, "T": 8192, "hd": 128, "dtype": "bf16", "causal": True, "precision": 1,
+           "plain_ms": 0.23, "plain_tflops": 600.0,
+           "splits": [{"nsplit": 2, "ms": 0.2, "speedup": 1.15, "tflops": 690.0, "max_abs_diff_O": 1e-4,
+                       "max_abs_diff_L": 2e-6},
+                      {"nsplit": 4, "ms": 0.18, "speedup": 1.28, "tflops": 766.0, "max_abs_diff_O": 3e-4,
+                       "max_abs_diff_L": 1e-6}]}
+    log = tmp_path / "split.log"
+    log.write_text(json.dumps(row) + "\n" + json.dumps({"split_workloads": 1, "device": "d", "arch": "gfx950",
+                                                        "cus": 256, "hip": "7"}) + "\n")
+    out = tmp_path / "split.md"
+    profile.split_report(str(log), str(out))
+    text = out.read_text()
+    table = [l for l in text.splitlines() if l.startswith("| B1 H4")]
+    assert len(table) == 1
+    assert "2 splits | 4 splits" in text
+    assert "766.0 (4 splits)" in table[0] and "3.00e-04" in table[0] and "2.00e-06" in table[0]
