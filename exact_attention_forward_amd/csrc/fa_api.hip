@@ -6,6 +6,9 @@
 #include "../../include/fa.h"
 #include "fa_launch.hpp"
 
+static_assert(fa::kErrUnsupported == FA_ERR_UNSUPPORTED && fa::kErrLaunch == FA_ERR_LAUNCH,
+              "launcher status codes must match the C ABI");
+
 namespace {
 
 struct Buf {

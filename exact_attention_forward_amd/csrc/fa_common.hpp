@@ -20,6 +20,11 @@
 
 namespace fa {
 
+// Status codes of the launchers: the C ABI's FA_ERR_UNSUPPORTED and
+// FA_ERR_LAUNCH (the ABI layer checks that the values agree).
+constexpr int kErrUnsupported = -3;
+constexpr int kErrLaunch = -5;
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));

@@ -8,7 +8,7 @@ int stage_f16(int stage, int hd, const void* args, bool causal, int prec, hipStr
   switch (hd) {
     case 64: return run_stage_hd<f16_t, 64>(stage, args, causal, prec, s);
     case 128: return run_stage_hd<f16_t, 128>(stage, args, causal, prec, s);
-    default: return -3;
+    default: return kErrUnsupported;
   }
 }
 
@@ -16,7 +16,7 @@ int delta_f16(int hd, const BwdArgs& a, hipStream_t s) {
   switch (hd) {
     case 64: return run_delta<f16_t, 64>(a, s);
     case 128: return run_delta<f16_t, 128>(a, s);
-    default: return -3;
+    default: return kErrUnsupported;
   }
 }
 

@@ -10,7 +10,7 @@ int stage_f32(int stage, int hd, const void* args, bool causal, hipStream_t s) {
     case 32: return run_stage_hd<float, 32>(stage, args, causal, 0, s);
     case 64: return run_stage_hd<float, 64>(stage, args, causal, 0, s);
     case 128: return run_stage_hd<float, 128>(stage, args, causal, 0, s);
-    default: return -3;
+    default: return kErrUnsupported;
   }
 }
 
@@ -21,7 +21,7 @@ int delta_f32(int hd, const BwdArgs& a, hipStream_t s) {
     case 32: return run_delta<float, 32>(a, s);
     case 64: return run_delta<float, 64>(a, s);
     case 128: return run_delta<float, 128>(a, s);
-    default: return -3;
+    default: return kErrUnsupported;
   }
 }
 
@@ -32,7 +32,7 @@ int unfused_f32(int hd, const UnfusedArgs& a, bool causal, hipStream_t s) {
     case 32: return run_unfused<32>(a, causal, s);
     case 64: return run_unfused<64>(a, causal, s);
     case 128: return run_unfused<128>(a, causal, s);
-    default: return -3;
+    default: return kErrUnsupported;
   }
 }
 

@@ -83,7 +83,7 @@ struct TileCfg<bf16_t, 128> {
   static constexpr int DKV_NW = 4, DKV_MR = 1, DKV_BQ = 64;
 };
 
-inline int launch_status() { return hipGetLastError() == hipSuccess ? 0 : -5; }
+inline int launch_status() { return hipGetLastError() == hipSuccess ? 0 : kErrLaunch; }
 
 // Compute units of the current device (cached per device id; calls from
 // several host threads may fill an entry concurrently with the same value).
@@ -122,7 +122,7 @@ constexpr bool is_16bit = std::is_same<TIn, bf16_t>::value || std::is_same<TIn, 
 template <typename TIn, int HD, bool CAUSAL, int PREC, int CONTROL = kCtlNone>
 int run_fwd(const FwdArgs& a, hipStream_t s) {
   if constexpr (CONTROL != kCtlNone && is_bf16<TIn>) {
-    return -3;  // the control variants are built for float32 and half inputs only
+    return kErrUnsupported;  // the control variants are built for float32 and half inputs only
   } else if constexpr (CONTROL == kCtlNone && is_16bit<TIn>) {
     using C = TileCfg32<HD>;
     auto* k = &fwd32_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC, C::FWD_MS>;
@@ -236,7 +236,7 @@ int run_fwd_split(const SplitArgs& sa, hipStream_t s) {
     hipLaunchKernelGGL((fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC>),
                        dim3((unsigned)(nqt * a.B * a.H), (unsigned)sa.nsplit), dim3(C::FWD_NW * 64), 0, s, a);
   }
-  if (launch_status()) return -5;
+  if (launch_status()) return kErrLaunch;
   MergeArgs m{a.o, a.lse, sa.o, sa.lse, a.B, a.H, a.T, sa.nsplit, n, nr};
   constexpr int RPB = 256 / (HD / 4);
   hipLaunchKernelGGL(merge_kernel<HD>, dim3((unsigned)((a.T + RPB - 1) / RPB), (unsigned)(a.B * a.H)), dim3(256), 0,

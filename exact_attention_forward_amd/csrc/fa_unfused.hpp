@@ -164,17 +164,17 @@ template <int HD>
 int run_unfused(const UnfusedArgs& a, bool causal, hipStream_t s) {
   const unsigned nt = (unsigned)((a.T + 63) / 64), bhn = (unsigned)(a.B * a.H);
   hipLaunchKernelGGL(scores_kernel<HD>, dim3(nt, nt, bhn), dim3(256), 0, s, a);
-  if (hipGetLastError() != hipSuccess) return -5;
+  if (hipGetLastError() != hipSuccess) return kErrLaunch;
   if (causal)
     hipLaunchKernelGGL(softmax_kernel<true>, dim3((unsigned)((a.T + 3) / 4), bhn), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(softmax_kernel<false>, dim3((unsigned)((a.T + 3) / 4), bhn), dim3(256), 0, s, a);
-  if (hipGetLastError() != hipSuccess) return -5;
+  if (hipGetLastError() != hipSuccess) return kErrLaunch;
   if (causal)
     hipLaunchKernelGGL((pv_kernel<HD, true>), dim3(nt, bhn), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((pv_kernel<HD, false>), dim3(nt, bhn), dim3(256), 0, s, a);
-  return hipGetLastError() == hipSuccess ? 0 : -5;
+  return hipGetLastError() == hipSuccess ? 0 : kErrLaunch;
 }
 
 }  // namespace fa
