@@ -61,10 +61,10 @@ def family(k: str) -> str | None:
 
 
 def kernel_durations(db: str) -> dict:
-    """Kernel name -> list of dispatch durations (ns)."""
+    """Kernel name -> list of dispatch durations (ns), in start order."""
     c = sqlite3.connect(db)
     out = collections.defaultdict(list)
-    for name, dur in c.execute("select name, duration from kernels"):
+    for name, dur in c.execute("select name, duration from kernels order by start"):
         out[name].append(float(dur))
     return out
 
@@ -82,13 +82,22 @@ def mean(x):
     return sum(x) / len(x) if x else float("nan")
 
 
-def trace_table(db: str) -> str:
+TRACE_STEPS = 20  # timed steps of the kernel-trace run
+
+
+def trace_table(db: str, last: int | None = None) -> str:
+    """Per-kernel calls, total and average duration; with ``last``, also the
+    average over each kernel's last ``last`` dispatches (the timed steps of a
+    bench run, after the warm-up ones)."""
     d = kernel_durations(db)
-    rows = [(k, len(v), sum(v) / 1e3, mean(v) / 1e3) for k, v in d.items() if family(k)]
+    rows = [(k, len(v), sum(v) / 1e3, mean(v) / 1e3, mean(v[-last:]) / 1e3 if last else None)
+            for k, v in d.items() if family(k)]
     tot = sum(r[2] for r in rows)
-    lines = ["| kernel | calls | total us | avg us | share % |", "|---|---|---|---|---|"]
-    for k, n, t, a in sorted(rows, key=lambda r: -r[2]):
-        lines.append(f"| `{short_name(k)}` | {n} | {t:.1f} | {a:.2f} | {100 * t / tot:.1f} |")
+    head = "| kernel | calls | total us | avg us |" + (f" avg us, last {last} calls |" if last else "") + " share % |"
+    lines = [head, "|---|---|---|---|" + ("---|" if last else "") + "---|"]
+    for k, n, t, a, al in sorted(rows, key=lambda r: -r[2]):
+        lines.append(f"| `{short_name(k)}` | {n} | {t:.1f} | {a:.2f} |" + (f" {al:.2f} |" if last else "") +
+                     f" {100 * t / tot:.1f} |")
     return "\n".join(lines)
 
 
@@ -143,8 +152,16 @@ def fused_requests(N: int, d: int, Br: int, causal: bool) -> dict:
     return {"G": G, "reads": N * d + 2 * kv_keys * d, "writes": N * d}
 
 
+def bench_kernels(log_path) -> dict:
+    """Per-kernel times the bench line of a run reports (its "kernels" field)."""
+    for line in Path(log_path).read_text().splitlines():
+        if line.startswith('{"metric"'):
+            return json.loads(line).get("kernels", {})
+    return {}
+
+
 def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
-           B=64, H=16, T=1024, hd=64, fwd_rows=128) -> None:
+           B=64, H=16, T=1024, hd=64, fwd_rows=128, trace_log=None) -> None:
     out = Path(out_dir)
     heads = B * H
     d = kernel_durations(trace_db)
@@ -200,7 +217,14 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
     lines = [f"# Kernel trace: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
              "Command (from the repository root on an MI355X, after `cd /tmp && export TMPDIR=/tmp`, paths absolute, $OUT a scratch directory):",
              "", "    rocprofv3 --kernel-trace --stats -d $OUT/prof_trace -o trace -- "
-             "python3 bench.py --no-cpu-baseline --steps 20", "", trace_table(trace_db)]
+             f"python3 bench.py --no-cpu-baseline --steps {TRACE_STEPS}", "",
+             f"The run makes 50 warm-up steps (the clock settles under load during them) and {TRACE_STEPS} timed "
+             f"ones; the last column averages each kernel over those {TRACE_STEPS} timed steps, the window the "
+             "bench line's per-kernel times come from.", "", trace_table(trace_db, TRACE_STEPS)]
+    bk = bench_kernels(trace_log) if trace_log else {}
+    if bk:
+        lines += ["", "The bench line of the same run (HIP events around each kernel over the timed steps): " +
+                  ", ".join(f"`{k}` {1e3 * v['ms']:.1f} us" for k, v in bk.items()) + "."]
     (out / "kernel_trace_gpt2m_bf16.md").write_text("\n".join(lines) + "\n")
 
     flops = {"fwd32_kernel": 4, "dq32_kernel": 6, "dkv32_kernel": 8}
@@ -556,7 +580,7 @@ def main(argv=None) -> int:
     elif a.what == "split":
         split_report(*a.db[:2])
     else:
-        report(*a.db[:6])
+        report(*a.db[:6], trace_log=a.db[6] if len(a.db) > 6 else None)
     return 0
 
 
