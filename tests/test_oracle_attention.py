@@ -189,3 +189,26 @@ def test_flops_convention():
     f = A.flops(64, 16, 1024, 64, True)
     assert f["fwd"] == 4 * 64 * 64 * 16 * 1024 * 1024 / 2
     assert f["total"] == pytest.approx(481.036e9, rel=1e-5)
+
+
+def test_causal_head_decomposes_into_single_query_problems():
+    """A causal row i is the unmasked single-query problem on keys 0..i; dK and dV are the sums of those
+    problems' gradients over the rows (the loss is a sum over rows).  The long-sequence GPU test relies on
+    this to check rows and key columns of heads too long for the full-head oracle."""
+    from exact_attention_forward_amd import inputs as I
+
+    c = I.make_case("decomp", 1, 1, 96, 16, I.F32, True, 5)
+    q, k, v, do = (c.head_f64(n, 0, 0) for n in ("q", "k", "v", "do"))
+    O, L, _ = A.head_forward(q, k, v, c.scale, True)
+    dQ, dK, dV, _ = A.head_backward(q, k, v, do, c.scale, True)
+    dK_sum, dV_sum = np.zeros_like(dK), np.zeros_like(dV)
+    for i in range(96):
+        o, l, _ = A.head_forward(q[i:i + 1], k[:i + 1], v[:i + 1], c.scale, False)
+        dq, dk, dv, _ = A.head_backward(q[i:i + 1], k[:i + 1], v[:i + 1], do[i:i + 1], c.scale, False)
+        np.testing.assert_allclose(o[0], O[i], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l[0], L[i], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dq[0], dQ[i], rtol=0, atol=1e-13)
+        dK_sum[:i + 1] += dk
+        dV_sum[:i + 1] += dv
+    np.testing.assert_allclose(dK_sum, dK, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dV_sum, dV, rtol=0, atol=1e-12)
