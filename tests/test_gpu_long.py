@@ -9,12 +9,13 @@ parity test (float32: 2e-5, with 1e-3 for dV at T >= 4096; 16-bit inputs: 2e-2).
 """
 import numpy as np
 import pytest
+import torch
 
 import exact_attention_forward_amd as fa
 from exact_attention_forward_amd import inputs as I
 from oracle import attention as oracle
 
-from gpu_util import BF16_TOL, F32_TOL, run_case
+from gpu_util import BF16_TOL, F32_TOL, run_case, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -70,3 +71,29 @@ def test_long_sequence_sampled(B, H, T, hd, dtype, prec, seed):
         tol = {n: BF16_TOL for n in worst}
     bad = {n: e for n, e in worst.items() if not e <= tol[n]}
     assert not bad, f"errors over tolerance: {bad} (all: {worst})"
+
+
+@pytest.mark.parametrize("nsplit", [5, 16])
+def test_long_sequence_split_forward_sampled(nsplit):
+    """The split-key forward at T = 65536 (partial outputs of 8.4M floats each in the workspace)."""
+    B, H, T, hd = 1, 2, 65536, 64
+    c = I.make_case(f"long_split_T{T}", B, H, T, hd, I.BF16, True, 34)
+    print(f"[long split] B{B} H{H} T{T} hd{hd} bf16 nsplit={nsplit}", flush=True)
+    q, k, v = (to_device(c, n) for n in ("q", "k", "v"))
+    o = torch.full((B, T, H, hd), float("nan"), device="cuda")
+    lse = torch.full((B, H, T), float("nan"), device="cuda")
+    ws = torch.full((nsplit * (B * T * H * hd + B * H * T),), float("nan"), device="cuda")
+    fa.check(fa.fa_forward_splitkv(q, k, v, o, lse, ws, B, H, T, hd, c.scale, 1, nsplit, fa.FA_BF16,
+                                   fa.FA_PREC_BF16, None))
+    torch.cuda.synchronize()
+    O_g, L_g = o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(O_g).all() and np.isfinite(L_g).all()
+    worst = {}
+    for h in range(H):
+        q_, k_, v_ = (c.head_f64(n, 0, h) for n in ("q", "k", "v"))
+        for i in [0, 13107, 32768, T - 2, T - 1]:
+            O, L, _ = oracle.head_forward(q_[i:i + 1], k_[:i + 1], v_[:i + 1], c.scale, False)
+            worst["O"] = max(worst.get("O", 0.0), float(np.abs(O_g[0, i, h] - O[0]).max()))
+            worst["L"] = max(worst.get("L", 0.0), float(abs(L_g[0, h, i] - L[0])))
+    print(f"[long split] nsplit={nsplit}: {worst}", flush=True)
+    assert all(e <= BF16_TOL for e in worst.values()), worst
