@@ -154,6 +154,34 @@ def test_constant_values_give_constant_output(dtype, prec, tol):
     assert float((out["O"] - 1).abs().max()) <= tol
 
 
+@pytest.mark.parametrize("dtype,prec,tol", [(I.F32, 0, F32_TOL), (I.BF16, fa.FA_PREC_BF16, BF16_TOL),
+                                             (I.F16, fa.FA_PREC_DEFAULT, BF16_TOL)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_give_closed_forms(dtype, prec, tol, causal):
+    # Q = 0: every visible score ties at 0, so P is uniform over the visible
+    # keys.  Then O_i is the mean of the visible values, L_i = ln(count), dQ_i =
+    # scale * sum_j P_ij (dP_ij - D_i) k_j, dK = 0 (dS rows sum to zero and q = 0),
+    # and dV_j = sum over rows i that see j of dO_i / count_i.  Checked against
+    # these closed forms directly, not against the oracle.
+    B, H, T, hd = 1, 2, 300, 64
+    c = I.make_case("zero_q", B, H, T, hd, dtype, causal, 12)
+    c.q = np.zeros_like(c.q)
+    out = run_case(c, prec)
+    for h in range(H):
+        v, do = c.head_f64("v", 0, h), c.head_f64("do", 0, h)
+        cnt = np.arange(1, T + 1, dtype=np.float64) if causal else np.full(T, float(T))
+        O = np.cumsum(v, axis=0) / cnt[:, None] if causal else np.broadcast_to(v.mean(axis=0), (T, hd))
+        L = np.log(cnt)
+        w = do / cnt[:, None]  # each row's upstream gradient spread over its visible keys
+        dV = np.cumsum(w[::-1], axis=0)[::-1] if causal else np.broadcast_to(w.sum(axis=0), (T, hd))
+        got = {n: (out[n][0, h] if n == "L" else out[n][0, :, h]).cpu().numpy().astype(np.float64)
+               for n in ("O", "L", "dK", "dV")}
+        err = {"O": np.abs(got["O"] - O).max(), "L": np.abs(got["L"] - L).max(), "dK": np.abs(got["dK"]).max(),
+               "dV": np.abs(got["dV"] - dV).max()}
+        print(f"[zero q] {dtype} causal={causal} h={h} {err}", flush=True)
+        assert all(e <= tol for e in err.values()), err
+
+
 def test_stages_equal_combined_backward():
     c = I.make_case("stages", 2, 3, 200, 64, I.BF16, True, 10)
     ref = run_case(c)
