@@ -481,6 +481,40 @@ def clock_report(db: str, out_md: str) -> None:
     Path(out_md).write_text("\n".join(lines) + "\n")
 
 
+UTIL_METRICS = ("MfmaUtil", "VALUBusy", "LDSBankConflict", "OccupancyPercent")
+
+
+def util_all_report(db: str, out_md: str) -> None:
+    """Matrix-core and vector-ALU use of every attention kernel of the C2, C3 and C4 workloads."""
+    c = sqlite3.connect(db)
+    per = collections.defaultdict(lambda: collections.defaultdict(dict))
+    dur = collections.defaultdict(dict)
+    for dis, name, cn, v, d in c.execute("select dispatch_id, kernel_name, counter_name, value, duration "
+                                         "from counters_collection"):
+        if family(name) is None or workload_of(name) is None:
+            continue
+        per[name][cn][dis] = per[name][cn].get(dis, 0.0) + float(v)
+        dur[name][dis] = float(d)
+    lines = ["# Matrix-core and vector-ALU use of every workload's kernels (MI355X)", "",
+             "Command (from the repository root on an MI355X, after `cd /tmp && export TMPDIR=/tmp`; $OUT is a "
+             "scratch directory):", "",
+             "    rocprofv3 --pmc " + " ".join(UTIL_METRICS) + " -d $OUT/all_util -o u -- python3 bench.py "
+             "--counters --workloads C2,C3,C4",
+             "    python -m exact_attention_forward_amd.profile util_all DB OUT_MD", "",
+             "rocprofv3's derived metrics, averaged over each kernel's dispatches (two steps per workload): "
+             "MfmaUtil = matrix-core busy cycles over (GPU-active cycles x SIMDs); VALUBusy = vector-ALU busy "
+             "share; LDSBankConflict = bank-conflict cycles over LDS-active cycles; OccupancyPercent = resident "
+             "waves over the maximum.  C2: float32 B64 H16 T1024 hd64; C3: bf16, same shape; C4: bf16 B4 H16 "
+             "T8192 hd128 with split operands.", "",
+             "| workload | kernel | mean us | " + " | ".join(f"{m} %" for m in UTIL_METRICS) + " |",
+             "|---|---|---|" + "---|" * len(UTIL_METRICS)]
+    for name in sorted(per, key=lambda n: (workload_of(n), -mean(list(dur[n].values())))):
+        vals = [mean(list(per[name][m].values())) if m in per[name] else float("nan") for m in UTIL_METRICS]
+        lines.append(f"| {workload_of(name)} | `{short_name(name)}` | {mean(list(dur[name].values())) / 1e3:.1f} | "
+                     + " | ".join(f"{x:.1f}" for x in vals) + " |")
+    Path(out_md).write_text("\n".join(lines) + "\n")
+
+
 def configs_report(log_path, out_md) -> None:
     """Markdown table of a ``bench.py --configs`` log (one JSON line per workload, then a summary line)."""
     recs, summary = [], {}
@@ -560,7 +594,7 @@ def split_report(log_path, out_md) -> None:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab", "configs", "traffic_all", "clock",
-                                     "split"))
+                                     "split", "util_all"))
     ap.add_argument("db", nargs="+")
     a = ap.parse_args(argv)
     if a.what == "trace":
@@ -579,6 +613,8 @@ def main(argv=None) -> int:
         clock_report(*a.db[:2])
     elif a.what == "split":
         split_report(*a.db[:2])
+    elif a.what == "util_all":
+        util_all_report(*a.db[:2])
     else:
         report(*a.db[:6], trace_log=a.db[6] if len(a.db) > 6 else None)
     return 0
