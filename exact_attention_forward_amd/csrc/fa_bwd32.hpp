@@ -42,7 +42,7 @@ template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int BC, bool FUSE
 __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : FA_DQ_OCC128) void dq32_kernel(BwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
-  constexpr int LD = HD + 8;
+  constexpr int LD = HD <= 64 ? HD + 8 : HD + 24;  // LDS row pitch (elements); see lds_ld
   constexpr int NDT = HD / 32;
   constexpr int NKS = HD / 16;
   constexpr int NKT = BC / 32;
@@ -260,7 +260,7 @@ template <typename TIn, int HD, bool CAUSAL, int PREC, int NW, int BQ>
 __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BK = NW * 32;
-  constexpr int LD = HD + 8;
+  constexpr int LD = HD <= 64 ? HD + 8 : HD + 24;  // LDS row pitch (elements); see lds_ld
   constexpr int NDT = HD / 32;
   constexpr int NKS = HD / 16;
   constexpr int NIT = BQ / 32;

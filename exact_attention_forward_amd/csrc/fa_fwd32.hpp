@@ -99,7 +99,7 @@ void fwd32_kernel(FwdArgs a) {
   // Persistent: the grid is sized to the resident workgroups and each loops over work items.
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32 * MS;
-  constexpr int LD = HD + 8;
+  constexpr int LD = HD <= 64 ? HD + 8 : HD + 24;  // LDS row pitch (elements); see lds_ld
   constexpr int NDT = HD / 32;  // 32-wide output tiles
   constexpr int NKS = HD / 16;  // product steps over the head dim
   constexpr int NKT = BC / 32;  // 32-key tiles per block
