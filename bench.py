@@ -474,8 +474,14 @@ def configs(args) -> int:
     work += [("C1", c, fa.FA_PREC_DEFAULT) for c in I.ragged_cases()]
     work += [("C2", lambda: I.gpt2m_case(I.F32), fa.FA_PREC_DEFAULT),
              ("C3", lambda: I.gpt2m_case(I.BF16), fa.FA_PREC_BF16),
+             ("C3-split", lambda: I.gpt2m_case(I.BF16), fa.FA_PREC_BF16X2),
              ("C3-f16", lambda: I.gpt2m_case(I.F16), fa.FA_PREC_DEFAULT),
-             ("C4", I.long_case, fa.FA_PREC_BF16X2)]
+             ("C4", I.long_case, fa.FA_PREC_BF16X2),
+             ("C4-single", I.long_case, fa.FA_PREC_BF16)]
+    # outputs graded against the bar: with P and dS rounded once to bfloat16 the
+    # long-context gradients exceed 2e-2 (reported, not graded; that workload
+    # runs with split operands)
+    graded = {"C4-single": ("O", "L")}
     label = device_label(dev)
     summary = []
     for cfg, case, prec in work:
@@ -495,7 +501,8 @@ def configs(args) -> int:
             heads = [heads[0], heads[len(heads) // 3], heads[2 * len(heads) // 3], heads[-1]]
         worst, t_oracle = cpu_baseline_heads(case, dict(O=o, L=lse, dQ=dq, dK=dk, dV=dv), heads)
         tol = 2e-5 if case.dtype == I.F32 else 2e-2
-        ok = all(e <= tol for e in worst.values())
+        names = graded.get(cfg, ("O", "L", "dQ", "dK", "dV"))
+        ok = all(worst[n] <= tol for n in names)
         dt = {I.F32: fa.FA_F32, I.BF16: fa.FA_BF16, I.F16: fa.FA_F16}[case.dtype]
 
         def fwd():
@@ -535,7 +542,7 @@ def configs(args) -> int:
         rec = {"config": cfg, "workload": case.name, "B": B, "H": H, "T": T, "hd": hd, "dtype": case.dtype,
                "causal": bool(case.causal), "precision": int(prec), "counted_gflop": round(counted / 1e9, 6),
                "times": times, "tflops": round(tflops, 3), "frac_of_peak": round(tflops / peak, 4),
-               "peak_tflops": peak, "parity": {"heads": len(heads), "tol": tol, "ok": ok,
+               "peak_tflops": peak, "parity": {"heads": len(heads), "tol": tol, "ok": ok, "graded": list(names),
                                                "max_abs_err": {n: float(f"{e:.3e}") for n, e in worst.items()}},
                "oracle_s_per_head": round(t_oracle, 4), "oracle_s_est": round(t_oracle * B * H, 2)}
         print(json.dumps(rec), flush=True)
@@ -548,56 +555,72 @@ def configs(args) -> int:
     return 0 if all(r["parity"]["ok"] for r in summary) else 1
 
 
+def _host_outputs(out):
+    """The GPU outputs copied to host float64 once, outside every timed region."""
+    import numpy as np
+
+    return {n: t.cpu().numpy().astype(np.float64) for n, t in out.items()}
+
+
+def _head_errors(host, b, h, ref, worst):
+    import numpy as np
+
+    for n, r in zip(("O", "L", "dQ", "dK", "dV"), ref):
+        g = host[n][b, h] if n == "L" else host[n][b, :, h]
+        worst[n] = max(worst.get(n, 0.0), float(np.abs(g - r).max()))
+
+
+def _oracle_head(case, b, h):
+    """(seconds, (O, L, dQ, dK, dV)) of the float64 oracle on one head; the timer covers only the oracle calls."""
+    from oracle import attention as oracle
+
+    qh, kh, vh, dh = (case.head_f64(n, b, h) for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    O, L, _ = oracle.head_forward(qh, kh, vh, case.scale, case.causal)
+    dQ, dK, dV, _ = oracle.head_backward(qh, kh, vh, dh, case.scale, case.causal)
+    return time.perf_counter() - t0, (O, L, dQ, dK, dV)
+
+
 def cpu_baseline_heads(case, out, heads):
     """The oracle on the given heads: worst error of each output against it, and the
     oracle's time for the first head (the CPU baseline of one workload)."""
-    import numpy as np
-
-    from oracle import attention as oracle
-
+    host = _host_outputs(out)
     worst, t_first = {}, None
     for b, h in heads:
-        qh, kh, vh, dh = (case.head_f64(n, b, h) for n in ("q", "k", "v", "do"))
-        t0 = time.perf_counter()
-        O, L, _ = oracle.head_forward(qh, kh, vh, case.scale, case.causal)
-        dQ, dK, dV, _ = oracle.head_backward(qh, kh, vh, dh, case.scale, case.causal)
-        if t_first is None:
-            t_first = time.perf_counter() - t0
-        for n, ref in (("O", O), ("L", L), ("dQ", dQ), ("dK", dK), ("dV", dV)):
-            g = out[n][b, h] if n == "L" else out[n][b, :, h]
-            worst[n] = max(worst.get(n, 0.0), float(np.abs(g.cpu().numpy().astype(np.float64) - ref).max()))
+        t, ref = _oracle_head(case, b, h)
+        t_first = t if t_first is None else t_first
+        _head_errors(host, b, h, ref, worst)
     return worst, t_first
 
 
 def cpu_baseline(case, out, budget_s: float):
-    """Time the float64 oracle on whole heads of the workload until the budget is spent."""
+    """Time the float64 oracle on whole heads of the workload until `budget_s` of oracle time is spent.
+
+    Only the oracle's own calls are timed: the GPU outputs are copied to the
+    host before, and each head is compared with them after, its timed calls.
+    """
     import numpy as np
 
-    from oracle import attention as oracle
-
-    host = host_label()
-    threads = host["blas_threads"] or host["cpu_count"] or 1
+    host_info = host_label()
+    threads = host_info["blas_threads"] or host_info["cpu_count"] or 1
+    host = _host_outputs(out)
     heads = [(b, h) for b in range(case.B) for h in range(case.H)]
     order = np.random.default_rng(0).permutation(len(heads))
-    done, worst = [], {}
-    t0 = time.perf_counter()
+    done, worst, el = 0, {}, 0.0
     for idx in order:
         b, h = heads[idx]
-        qh, kh, vh, dh = (case.head_f64(n, b, h) for n in ("q", "k", "v", "do"))
-        O, L, _ = oracle.head_forward(qh, kh, vh, case.scale, case.causal)
-        dQ, dK, dV, _ = oracle.head_backward(qh, kh, vh, dh, case.scale, case.causal)
-        done.append((b, h))
-        for n, ref in (("O", O), ("L", L), ("dQ", dQ), ("dK", dK), ("dV", dV)):
-            g = out[n][b, h] if n == "L" else out[n][b, :, h]
-            worst[n] = max(worst.get(n, 0.0), float(np.abs(g.cpu().numpy().astype(np.float64) - ref).max()))
-        if time.perf_counter() - t0 >= budget_s:
+        t, ref = _oracle_head(case, b, h)
+        el += t
+        done += 1
+        _head_errors(host, b, h, ref, worst)
+        if el >= budget_s:
             break
-    el = time.perf_counter() - t0
-    flops = 14 * case.hd * case.T * case.T / 2 * len(done)
+    flops = 14 * case.hd * case.T * case.T / 2 * done
     base = {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(done)} of {case.B * case.H} heads (float64 NumPy, fwd+bwd per head), {el:.1f} s",
-            "cpu_model": host["cpu_model"]}
-    parity = {"heads": len(done), "max_abs_err": {k: float(f"{v:.3e}") for k, v in worst.items()}, "tol": 2e-2,
+            "sample": f"{done} of {case.B * case.H} heads (float64 NumPy, fwd+bwd per head), {el:.1f} s of oracle time",
+            "cpu_model": host_info["cpu_model"], "cpu_count": host_info["cpu_count"],
+            "blas_threads": host_info["blas_threads"]}
+    parity = {"heads": done, "max_abs_err": {k: float(f"{v:.3e}") for k, v in worst.items()}, "tol": 2e-2,
               "ok": all(v <= 2e-2 for v in worst.values())}
     return base, parity
 

@@ -2,7 +2,10 @@
 
 torch supplies device memory and the current stream; every step of the
 computation runs in the HIP library.  Inputs are contiguous [B, T, H, hd]
-device tensors of dtype float32, bfloat16 or float16; outputs are float32.
+device tensors of one dtype (float32, bfloat16 or float16) on one device;
+outputs are float32.  Every tensor argument is checked here, before the
+library is called: the C ABI sees only raw pointers and would read a tensor
+of another dtype or size out of bounds.
 """
 from __future__ import annotations
 
@@ -10,8 +13,8 @@ import math
 
 import torch
 
-from ._binding import (FA_BF16, FA_F16, FA_F32, FA_PREC_DEFAULT, check, fa_backward, fa_backward_delta, fa_backward_dkv,
-                       fa_backward_dq, fa_forward)
+from . import _binding as _b
+from ._binding import FA_BF16, FA_F16, FA_F32, FA_PREC_DEFAULT, check
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -24,37 +27,75 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported input dtype {t.dtype}")
 
 
-def _shape(q: torch.Tensor, *others: torch.Tensor):
-    if q.dim() != 4:
+def _on_device(t: torch.Tensor) -> bool:
+    """True for a GPU tensor (the library takes device pointers only)."""
+    return bool(t.is_cuda)
+
+
+def _inputs(q: torch.Tensor, *others: torch.Tensor):
+    """[B, T, H, hd] inputs: one shape, one dtype, one device, contiguous, on the GPU."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("expected [B, T, H, hd] tensors")
+    _dtype_code(q)
     for t in (q, *others):
-        if t.shape != q.shape or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("inputs must be contiguous device tensors of one shape")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("inputs must be torch tensors")
+        if t.dtype != q.dtype:
+            raise TypeError(f"inputs must share one dtype: {t.dtype} vs {q.dtype}")
+        if t.shape != q.shape:
+            raise ValueError(f"inputs must share one shape: {tuple(t.shape)} vs {tuple(q.shape)}")
+        if not _on_device(t) or t.device != q.device:
+            raise ValueError("inputs must be device tensors on one device")
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
     B, T, H, hd = q.shape
     return B, T, H, hd
 
 
+def _f32(t, shape, device, name: str) -> None:
+    """A float32 tensor of the given shape, contiguous, on `device`."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not _on_device(t) or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device)
+
+
 def forward(q, k, v, scale: float | None = None, causal: bool = True, prec: int = FA_PREC_DEFAULT, stream=None):
     """Returns (o [B, T, H, hd] float32, lse [B, H, T] float32)."""
-    B, T, H, hd = _shape(q, k, v)
+    B, T, H, hd = _inputs(q, k, v)
     scale = 1.0 / math.sqrt(hd) if scale is None else scale
     o = torch.empty((B, T, H, hd), device=q.device, dtype=torch.float32)
     lse = torch.empty((B, H, T), device=q.device, dtype=torch.float32)
-    stream = torch.cuda.current_stream(q.device) if stream is None else stream
-    check(fa_forward(q, k, v, o, lse, B, H, T, hd, scale, causal, _dtype_code(q), prec, stream))
+    stream = _stream(q.device) if stream is None else stream
+    check(_b.fa_forward(q, k, v, o, lse, B, H, T, hd, scale, causal, _dtype_code(q), prec, stream))
     return o, lse
 
 
 def backward(q, k, v, o, lse, do, scale: float | None = None, causal: bool = True, prec: int = FA_PREC_DEFAULT,
              stream=None):
-    """Returns (dq, dk, dv [B, T, H, hd] float32, delta [B, H, T] float32)."""
-    B, T, H, hd = _shape(q, k, v, do)
+    """Returns (dq, dk, dv [B, T, H, hd] float32, delta [B, H, T] float32).
+
+    o and lse are the forward's outputs: float32 [B, T, H, hd] and [B, H, T].
+    """
+    B, T, H, hd = _inputs(q, k, v, do)
+    _f32(o, (B, T, H, hd), q.device, "o")
+    _f32(lse, (B, H, T), q.device, "lse")
     scale = 1.0 / math.sqrt(hd) if scale is None else scale
     dq = torch.empty((B, T, H, hd), device=q.device, dtype=torch.float32)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
     delta = torch.empty((B, H, T), device=q.device, dtype=torch.float32)
-    stream = torch.cuda.current_stream(q.device) if stream is None else stream
-    check(fa_backward(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, T, hd, scale, causal, _dtype_code(q), prec,
-                      stream))
+    stream = _stream(q.device) if stream is None else stream
+    check(_b.fa_backward(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, T, hd, scale, causal, _dtype_code(q), prec,
+                         stream))
     return dq, dk, dv, delta

@@ -360,9 +360,12 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
     // tiles: A(t) = the S and dP products, B(t) = P and dS in registers (VALU
     // and exp), C(t) = the dV and dK products.  The order A(t+1), B(t), C(t)
     // keeps independent matrix and vector work next to each other.
+    // FIRST: the first 32-row tile to visit; under the causal mask the tiles
+    // before it lie wholly above this wave's first key (every P is zero).
     auto block = [&](const bf16_t* cQ, const bf16_t* cG, const float* cL, const float* cD, const int q0,
-                     auto masked) {
+                     auto masked, auto first) {
       constexpr bool MASK = decltype(masked)::value;
+      constexpr int FIRST = decltype(first)::value;
       f32x16 s[2], dp[2];
       auto stage_a = [&](int it, f32x16& sa, f32x16& da) {
         sa = zero16();
@@ -373,9 +376,9 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
           da = mma32(ld_row32<V8>(cG, LD, 32 * it, 16 * ks, n, h), vf[ks], da);
         }
       };
-      stage_a(0, s[0], dp[0]);
+      stage_a(FIRST, s[FIRST & 1], dp[FIRST & 1]);
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
+      for (int it = FIRST; it < NIT; ++it) {
         f32x16& sc = s[it & 1];
         f32x16& dc = dp[it & 1];
         if (it + 1 < NIT) stage_a(it + 1, s[(it + 1) & 1], dp[(it + 1) & 1]);
@@ -434,10 +437,19 @@ __global__ __launch_bounds__(NW * 64, HD <= 64 ? 2 : 1) void dkv32_kernel(BwdArg
       }
       if (fw >= 0) fetch(fw, fqb);
       if (!CAUSAL || q0 + BQ - 1 >= c0) {
-        if (CAUSAL && q0 < c0 + 31)
-          block(sQ[buf], sG[buf], sL[buf], sD[buf], q0, std::true_type{});
-        else
-          block(sQ[buf], sG[buf], sL[buf], sD[buf], q0, std::false_type{});
+        if (CAUSAL && q0 < c0 + 31) {
+          // tiles wholly above the wave's first key are skipped (c0 - q0 is a
+          // multiple of 32; the block is visited only if its last tile is live)
+          const int it0 = q0 >= c0 ? 0 : (c0 - q0) >> 5;
+          static_assert(NIT <= 4, "first-tile dispatch covers up to four tiles");
+          auto masked = [&](auto f) { block(sQ[buf], sG[buf], sL[buf], sD[buf], q0, std::true_type{}, f); };
+          if (it0 == 0) masked(std::integral_constant<int, 0>{});
+          if constexpr (NIT > 1) if (it0 == 1) masked(std::integral_constant<int, 1>{});
+          if constexpr (NIT > 2) if (it0 == 2) masked(std::integral_constant<int, 2>{});
+          if constexpr (NIT > 3) if (it0 == 3) masked(std::integral_constant<int, 3>{});
+        } else {
+          block(sQ[buf], sG[buf], sL[buf], sD[buf], q0, std::false_type{}, std::integral_constant<int, 0>{});
+        }
       }
       if (more || wn >= 0) commit(buf ^ 1);
       __syncthreads();

@@ -2,7 +2,9 @@
 // units.  Tile shapes per (input type, head dim) live in TileCfg.
 #pragma once
 #include <atomic>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "fa_bwd.hpp"
 #include "fa_bwd32.hpp"
@@ -99,17 +101,37 @@ inline int device_cus() {
   return n;
 }
 
+// Resident workgroups per compute unit of one kernel on the current device.
+// The cache is keyed by (device, kernel address, block size): kernels of one
+// function type (every forward instantiation, say) have different register
+// and LDS footprints, so each needs its own entry.
+inline int resident_per_cu(const void* kernel, int threads) {
+  struct Entry {
+    int dev;
+    const void* kernel;
+    int threads;
+    int per_cu;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (const Entry& e : cache)
+      if (e.dev == dev && e.kernel == kernel && e.threads == threads) return e.per_cu;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
+  std::lock_guard<std::mutex> g(mu);
+  cache.push_back(Entry{dev, kernel, threads, n});
+  return n;
+}
+
 // Grid for a persistent kernel: every resident workgroup slot, at most one per item.
 template <typename K>
 inline long persistent_grid(K kernel, int threads, long items) {
-  // resident workgroups per compute unit, one value per kernel instantiation
-  // (a function-local static is initialised once, also under concurrent calls)
-  static const int per_cu = [&] {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
-    return n;
-  }();
-  const long slots = (long)per_cu * device_cus();
+  const long slots = (long)resident_per_cu(reinterpret_cast<const void*>(kernel), threads) * device_cus();
   return items < slots ? items : slots;
 }
 

@@ -174,11 +174,9 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
                                                     "hbm_bytes_per_launch")} for k, v in tr["kernels"].items()}}
     (out / "traffic.json").write_text(json.dumps(tr_json, indent=1) + "\n")
 
-    # compulsory bytes per launch: every tensor once (bf16 inputs, f32 O / L / D / grads)
-    E, nd = heads * T * hd, heads * T
-    comp = {"fwd32_kernel": (3 * 2 * E, 4 * E + 4 * nd),
-            "dq32_kernel": (4 * 2 * E + 4 * E + 4 * nd, 4 * E + 4 * nd),
-            "dkv32_kernel": (4 * 2 * E + 8 * nd, 8 * E)}
+    # compulsory bytes per launch: every tensor once (bf16 inputs, f32 O / L / D / grads; D fused into dQ)
+    comp = {fam: compulsory_bytes(fam, B, H, T, hd, 2, fused_d=True)
+            for fam in ("fwd32_kernel", "dq32_kernel", "dkv32_kernel")}
     fr = fused_requests(T, hd, fwd_rows, True)
     fr_nc = fused_requests(T, hd, fwd_rows, False)
     lines = [f"# HBM traffic per launch: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
@@ -356,29 +354,45 @@ def suffix_rows(N: int, bk: int, bq: int) -> int:
     return sum((nqb - (t * bk) // bq) * bq for t in range(_cdiv(N, bk)))
 
 
+def compulsory_bytes(fam: str, B: int, H: int, T: int, hd: int, e: int, fused_d: bool) -> tuple:
+    """(read, write) bytes of one launch that reads every input tensor once and writes every output once.
+
+    Inputs q, k, v, dO have e bytes per element; O, L, D and the gradients are
+    float32.  The forward reads q, k, v and writes O and L.  The dQ kernel reads
+    q, k, v, dO and L, plus O when it computes D itself (fused_d; then it also
+    writes D) or D otherwise, and writes dQ.  The dK/dV kernel reads q, k, v,
+    dO, L and D and writes dK and dV.  The D pre-pass reads O and dO and writes D.
+    """
+    n, r = B * H * T * hd, B * H * T
+    if fam in ("fwd32_kernel", "fwd_kernel"):
+        return 3 * n * e, 4 * n + 4 * r
+    if fam in ("dq32_kernel", "dq_kernel"):
+        if fused_d:
+            return 4 * n * e + 4 * n + 4 * r, 4 * n + 4 * r
+        return 4 * n * e + 8 * r, 4 * n
+    if fam in ("dkv32_kernel", "dkv_kernel"):
+        return 4 * n * e + 8 * r, 8 * n
+    if fam == "delta_kernel":
+        return n * e + 4 * n, 4 * r
+    raise KeyError(fam)
+
+
 def kernel_model(wl: str, fam: str) -> dict:
     """Requested (L2) and compulsory bytes per launch of one kernel of a causal workload."""
     w = WORKLOADS[wl]
     N, d, e, heads = w["T"], w["hd"], w["e"], w["B"] * w["H"]
     nd = N * d
+    comp_r, wr = compulsory_bytes(fam, w["B"], w["H"], N, d, e, w["fused_d"])
     if fam in ("fwd32_kernel", "fwd_kernel"):
         req_r = nd * e + 2 * d * e * prefix_keys(N, *w["fwd"])
-        comp_r, wr = 3 * nd * e, 4 * nd + 4 * N
     elif fam in ("dq32_kernel", "dq_kernel"):
         extra = 4 * nd + 4 * N if w["fused_d"] else 8 * N  # O and L (D computed) or L and D
         req_r = 2 * nd * e + extra + 2 * d * e * prefix_keys(N, *w["dq"])
-        comp_r = 4 * nd * e + extra
-        wr = 4 * nd + (4 * N if w["fused_d"] else 0)
     elif fam in ("dkv32_kernel", "dkv_kernel"):
         req_r = 2 * nd * e + (2 * d * e + 8) * suffix_rows(N, *w["dkv"])
-        comp_r, wr = 4 * nd * e + 8 * N, 8 * nd
-    elif fam == "delta_kernel":
-        req_r = comp_r = 4 * nd + nd * e
-        wr = 4 * N
-    else:
-        raise KeyError(fam)
-    return {"req_read": req_r * heads, "comp_read": comp_r * heads, "write": wr * heads,
-            "pairs": heads * N * N / 2}
+    else:  # delta_kernel
+        req_r = 4 * nd + nd * e
+    return {"req_read": req_r * heads, "comp_read": comp_r, "write": wr, "pairs": heads * N * N / 2}
 
 
 def workload_of(kernel: str) -> str | None:

@@ -43,27 +43,34 @@ def rows_checked(N: int) -> np.ndarray:
     return np.arange(N) if N <= 1024 else np.arange(64)
 
 
-def reference_and_bound(q, k, v, scale: float, rows=None):
-    """One head, no mask.  q, k, v: [N, d] (the exact stored values).
+def reference_and_bound(q, k, v, scale: float, rows=None, causal: bool = False):
+    """One head.  q, k, v: [N, d] (the exact stored values).
 
     Returns (ref [R, d], bound [R, d]) for the given rows (default: all).
+    With ``causal`` row i sees keys j <= i only, and every term of the bound
+    is taken over those keys: K is the count of visible keys, delta and e their
+    largest values, the floor their largest |v|.  Row i of the causal bound is
+    therefore the unmasked bound of the problem truncated to keys 0..i.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     N, d = q.shape
     rows = np.arange(N) if rows is None else np.asarray(rows)
-    s = scale * (q[rows] @ k.T)
+    vis = np.arange(N)[None, :] <= rows[:, None] if causal else np.ones((len(rows), N), bool)
+    s = np.where(vis, scale * (q[rows] @ k.T), -np.inf)
     m = s.max(axis=1)
     x = s - m[:, None]
-    w = np.exp(x)
+    w = np.where(vis, np.exp(x), 0.0)
     p = w / w.sum(axis=1)[:, None]
     ref = p @ v
-    delta = gamma(d + 1) * scale * (np.abs(q[rows]) @ np.abs(k).T)
-    e = (3.0 + 2.0 * np.abs(x)) * ULP
-    fac = 2.0 * (np.exp(2.0 * delta.max(axis=1) + 2.0 * e.max(axis=1)) - 1.0 + gamma(N))
-    floor = N * 2.0 ** -126 * np.abs(v).max(axis=0)
-    bound = fac[:, None] * (p @ np.abs(v)) + floor[None, :]
+    delta = np.where(vis, gamma(d + 1) * scale * (np.abs(q[rows]) @ np.abs(k).T), 0.0)
+    e = np.where(vis, (3.0 + 2.0 * np.abs(np.where(vis, x, 0.0))) * ULP, 0.0)
+    K = vis.sum(axis=1)
+    fac = 2.0 * (np.exp(2.0 * delta.max(axis=1) + 2.0 * e.max(axis=1)) - 1.0 + np.array([gamma(int(n)) for n in K]))
+    vmax = np.array([np.abs(v[vis[r]]).max(axis=0) for r in range(len(rows))])
+    floor = K[:, None] * 2.0 ** -126 * vmax
+    bound = fac[:, None] * (p @ np.abs(v)) + floor
     return ref, bound
 
 

@@ -108,39 +108,3 @@ def over_theta(kind: str, N: int, d: int, B: int, elements: int) -> float:
 def score_share(N: int, d: int, B: int) -> float:
     u = closed_unfused(N, d, B)
     return 4 * N * N / (u["globalReads"] + u["globalWrites"])
-
-
-# ---------------------------------------------------------------------------
-# Hot path (this library's kernels): counted work and compulsory bytes.
-# ---------------------------------------------------------------------------
-
-def visible_pairs(T: int, causal: bool) -> int:
-    """Exact number of (query, visible key) pairs of one head."""
-    return T * (T + 1) // 2 if causal else T * T
-
-
-def counted_pairs(B: int, H: int, T: int, causal: bool) -> float:
-    """Pairs as the throughput metric counts them: B H T^2, halved when causal."""
-    return B * H * T * T * (0.5 if causal else 1.0)
-
-
-def kernel_flops(B: int, H: int, T: int, hd: int, causal: bool) -> dict:
-    """Matrix-product flops each kernel must execute per launch, 2*hd per product per pair.
-
-    forward: S and P.V (4 hd); dQ kernel: S, dP and dQ (6 hd); dK/dV kernel:
-    S, dP, dV and dK (8 hd).  The metric's counted total is 14 hd per pair.
-    """
-    p = counted_pairs(B, H, T, causal)
-    return {"fwd": 4 * hd * p, "dq": 6 * hd * p, "dkv": 8 * hd * p, "counted_total": 14 * hd * p}
-
-
-def compulsory_bytes(B: int, H: int, T: int, hd: int, e_in: int) -> dict:
-    """Bytes each kernel must move at least once (inputs read once, outputs written once)."""
-    n = B * H * T * hd
-    r = B * H * T
-    return {
-        "fwd": 3 * n * e_in + 4 * n + 4 * r,             # q, k, v in; O, L out
-        "delta": n * e_in + 4 * n + 4 * r,               # dO, O in; D out
-        "dq": 4 * n * e_in + 8 * r + 4 * n,              # q, k, v, dO, L, D in; dQ out
-        "dkv": 4 * n * e_in + 8 * r + 8 * n,             # q, k, v, dO, L, D in; dK, dV out
-    }

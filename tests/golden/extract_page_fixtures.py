@@ -1,21 +1,24 @@
 """Write the page-printed values used as oracle pins into tests/golden/*.json.
 
-Reads the text of the "Lesson K23, fused attention" facts page (a single JSON
-record) from the reference copy at /root/reference/PAPER.md and keeps only
-numbers and field names.  Run once; the outputs are committed, and no test
-reads the reference at run time.
+Reads the text of the "Lesson K23 fused attention" facts page (a single JSON
+record: blocks traffic.rows, controls.vector, controls.checker, probe.heads and
+correctness.rows) from a local text copy of the page named on the command
+line, and keeps only numbers and field names.  Run once:
+
+    python tests/golden/extract_page_fixtures.py PAGE_TEXT_FILE
+
+The outputs are committed; no test reads the page text at run time.
 """
 import json
 import sys
 from pathlib import Path
 
-SRC = Path("/root/reference/PAPER.md")
 OUT = Path(__file__).resolve().parent
 PAGE = "Lesson K23 'fused attention' facts page"
 
 
-def page_record() -> dict:
-    for line in SRC.read_text().splitlines():
+def page_record(src: Path) -> dict:
+    for line in src.read_text().splitlines():
         line = line.strip()
         if line.startswith("{") and '"traffic"' in line:
             return json.loads(line)
@@ -23,7 +26,9 @@ def page_record() -> dict:
 
 
 def main() -> None:
-    rec = page_record()
+    if len(sys.argv) != 2:
+        sys.exit("usage: extract_page_fixtures.py PAGE_TEXT_FILE")
+    rec = page_record(Path(sys.argv[1]))
     keep = ["N", "d", "B", "kind", "globalReads", "globalWrites", "fma", "exps", "barriers", "sharedReads",
             "sharedWrites", "globalBytes", "extraMemoryBytes", "sharedPerWorkgroupBytes", "overTheta", "scoreShare",
             "overFused"]

@@ -1,0 +1,100 @@
+"""Second checks of the GPU results that do not go through the oracle's own output (needs an MI355X).
+
+* The lesson's per-output error bound ("Lesson K23 fused attention" facts
+  page, block correctness.about; restricted to the keys a causal row sees) on
+  every float32 workload: tiny (both masks), ragged, and sampled heads of the
+  GPT-2-medium shape.
+* The gradient's column sums, which the mathematics fixes at any size ("Flash
+  Attention 2 -- backward pass notes", section "The math (FA2 backward with
+  recompute)": the rows of dS sum to zero and the rows of P to one):
+  sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, over every head of the
+  GPT-2-medium shape in bfloat16.
+* Both operand-precision modes at both bfloat16 workloads: the split operand
+  at the GPT-2-medium shape, and the single bfloat16 rounding of P and dS at
+  the long-context shape, where its gradient error exceeds the 2e-2 bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_forward_amd as fa
+from exact_attention_forward_amd import inputs as I
+from oracle import checker
+
+from gpu_util import BF16_TOL, assert_within, head_errors, run_case
+
+pytestmark = pytest.mark.gpu
+
+
+def bound_check(case, out, heads):
+    worst = 0.0
+    for b, h in heads:
+        q, k, v = (case.head_f64(n, b, h) for n in ("q", "k", "v"))
+        ref, bound = checker.reference_and_bound(q, k, v, case.scale, causal=case.causal)
+        r = checker.check(out["O"][b, :, h].cpu().numpy(), ref, bound)
+        print(f"[bound] {case.name} b{b} h{h} causal={case.causal} ok={r['ok']} mismatches={r['mismatches']} "
+              f"maxRatio={r['maxRatio']:.3f}", flush=True)
+        assert r["ok"], (case.name, b, h, r)
+        worst = max(worst, r["maxRatio"])
+    return worst
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_within_lesson_bound(causal):
+    c = I.tiny_case(causal)
+    bound_check(c, run_case(c), [(0, 0)])
+
+
+@pytest.mark.parametrize("idx", range(len(I.RAGGED_SHAPES)))
+def test_ragged_within_lesson_bound(idx):
+    c = I.ragged_cases()[idx]
+    bound_check(c, run_case(c), [(b, h) for b in range(c.B) for h in range(c.H)])
+
+
+def test_gpt2m_f32_within_lesson_bound():
+    c = I.gpt2m_case(I.F32)
+    bound_check(c, run_case(c), [(0, 0), (63, 15), (17, 5)])
+
+
+def test_gpt2m_bf16_gradient_column_sums():
+    c = I.gpt2m_case(I.BF16)
+    out = run_case(c, fa.FA_PREC_BF16)
+    sum_dk = out["dK"].double().sum(dim=1)  # [B, H, hd]
+    sum_dv = out["dV"].double().sum(dim=1)
+    sum_do = torch.from_numpy(c.f64("do").sum(axis=1)).cuda()
+    ek = float(sum_dk.abs().max())
+    ev = float((sum_dv - sum_do).abs().max())
+    print(f"[sums] all {c.B * c.H} heads: max |sum_j dK_j| = {ek:.3e}, "
+          f"max |sum_j dV_j - sum_i dO_i| = {ev:.3e}", flush=True)
+    assert ek <= BF16_TOL and ev <= BF16_TOL
+
+
+def test_gpt2m_bf16_split_operands_sampled():
+    c = I.gpt2m_case(I.BF16)
+    out = run_case(c, fa.FA_PREC_BF16X2)
+    worst = {}
+    for b, h in [(0, 0), (63, 15), (17, 5)]:
+        for n, e in head_errors(c, out, b, h).items():
+            worst[n] = max(worst.get(n, 0.0), e)
+    print(f"[prec] {c.name} FA_PREC_BF16X2 " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()), flush=True)
+    assert_within(worst, BF16_TOL, c.name)
+    assert_within(worst, 1e-3, c.name + " split operands")
+
+
+def test_long_single_rounding_exceeds_the_bar_only_in_gradients():
+    """B4 H16 T8192 hd128 with 1% key outliers and P, dS rounded once to bfloat16.
+
+    The forward stays within 2e-2; the gradients do not (long rows sum many
+    rounded weights), which is why this workload runs with split operands.
+    Held to the size the rounding analysis of this workload predicts: about
+    0.1 at most.
+    """
+    c = I.long_case()
+    out = run_case(c, fa.FA_PREC_BF16)
+    worst = {}
+    for b, h in [(0, 0), (3, 15)]:
+        for n, e in head_errors(c, out, b, h).items():
+            worst[n] = max(worst.get(n, 0.0), e)
+    print(f"[prec] {c.name} FA_PREC_BF16 " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()), flush=True)
+    assert_within(worst, BF16_TOL, c.name + " forward", names=("O", "L"))
+    assert_within(worst, 0.25, c.name + " gradients", names=("dQ", "dK", "dV"))

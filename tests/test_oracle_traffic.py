@@ -44,12 +44,3 @@ def test_unfused_minus_fused_is_four_score_tables():
     for N, d, B in [(64, 16, 128), (1024, 64, 32), (4096, 16, 128)]:
         u, f = TR.closed_unfused(N, d, B), TR.closed_fused(N, d, B)
         assert (u["globalReads"] + u["globalWrites"]) - (f["globalReads"] + f["globalWrites"]) == 4 * N * N
-
-
-def test_hot_path_counts():
-    f = TR.kernel_flops(64, 16, 1024, 64, True)
-    assert f["fwd"] + f["dq"] + f["dkv"] == pytest.approx(18 * 64 * 64 * 16 * 1024 * 1024 / 2)
-    assert f["counted_total"] == pytest.approx(481.036e9, rel=1e-5)
-    assert TR.visible_pairs(5, True) == 15 and TR.visible_pairs(5, False) == 25
-    b = TR.compulsory_bytes(64, 16, 1024, 64, 2)
-    assert b["fwd"] == 3 * 2 * 2**26 + 4 * 2**26 + 4 * 2**20

@@ -71,3 +71,48 @@ def test_split_report_table(tmp_path):
     assert len(table) == 1
     assert "2 splits | 4 splits" in text
     assert "766.0 (4 splits)" in table[0] and "3.00e-04" in table[0] and "2.00e-06" in table[0]
+
+
+# Each tensor of the backward interface with its element count per head (T rows
+# of hd values, or T scalars) and whether it is an input of dtype e or float32.
+def _inventory(T, hd, e):
+    rows = T * hd
+    return {"q": rows * e, "k": rows * e, "v": rows * e, "dO": rows * e, "O": rows * 4, "L": T * 4, "D": T * 4,
+            "dQ": rows * 4, "dK": rows * 4, "dV": rows * 4}
+
+
+# What each kernel reads and writes, tensor by tensor.
+_ROLES = {
+    "fwd32_kernel": (("q", "k", "v"), ("O", "L")),
+    "dq32_kernel": (("q", "k", "v", "dO", "L", "D"), ("dQ",)),
+    "dq32_kernel+D": (("q", "k", "v", "dO", "L", "O"), ("dQ", "D")),
+    "dkv32_kernel": (("q", "k", "v", "dO", "L", "D"), ("dK", "dV")),
+    "delta_kernel": (("O", "dO"), ("D",)),
+}
+
+
+@pytest.mark.parametrize("shape", [(64, 16, 1024, 64, 2), (64, 16, 1024, 64, 4), (4, 16, 8192, 128, 2),
+                                   (2, 3, 300, 32, 4)])
+@pytest.mark.parametrize("kernel", sorted(_ROLES))
+def test_compulsory_bytes_count_each_tensor_once(shape, kernel):
+    B, H, T, hd, e = shape
+    inv = _inventory(T, hd, e)
+    reads, writes = _ROLES[kernel]
+    fam, fused = kernel.split("+")[0], kernel.endswith("+D")
+    r, w = P.compulsory_bytes(fam, B, H, T, hd, e, fused_d=fused)
+    assert r == B * H * sum(inv[t] for t in reads)
+    assert w == B * H * sum(inv[t] for t in writes)
+
+
+def test_compulsory_bytes_match_the_gpt2_medium_figures():
+    # B64 H16 T1024 hd64 bf16: forward 0.675 GB; backward D pre-pass 0.407, dQ 0.814 and dK/dV 1.082 GB
+    gb = lambda fam, fused=False: sum(P.compulsory_bytes(fam, 64, 16, 1024, 64, 2, fused)) / 1e9
+    assert round(gb("fwd32_kernel"), 3) == 0.675
+    assert round(gb("delta_kernel"), 3) == 0.407
+    assert round(gb("dq32_kernel"), 3) == 0.814
+    assert round(gb("dkv32_kernel"), 3) == 1.082
+    # D fused into the dQ kernel: the pre-pass's second read of dO and the dQ kernel's read of D disappear
+    n, r = 64 * 16 * 1024 * 64, 64 * 16 * 1024
+    assert gb("dq32_kernel", True) == pytest.approx(gb("dq32_kernel") + gb("delta_kernel") - (2 * n + 4 * r) / 1e9)
+    assert P.kernel_model("C3", "dq32_kernel")["comp_read"] == P.compulsory_bytes("dq32_kernel", 64, 16, 1024, 64, 2,
+                                                                                  True)[0]
