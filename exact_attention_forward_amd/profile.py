@@ -607,10 +607,94 @@ def split_report(log_path, out_md) -> None:
     Path(out_md).write_text("\n".join(lines) + "\n")
 
 
+def kernel_resources(asm_path: str) -> dict:
+    """Registers, LDS bytes and block size of every kernel in a device assembly file (its metadata block)."""
+    import re
+
+    text = Path(asm_path).read_text()
+    meta = text[text.index("amdhsa.kernels:"):]
+    out = {}
+    for chunk in re.split(r"\n  - \.", meta)[1:]:
+        f = dict(re.findall(r"\.?([a-z_]+):\s+(\S+)", "." + chunk))
+        if "name" in f and "vgpr_count" in f:
+            out[f["name"]] = {"vgpr": int(f["vgpr_count"]), "agpr": int(f.get("agpr_count", 0)),
+                              "lds": int(f.get("group_segment_fixed_size", 0)),
+                              "block": int(f.get("max_flat_workgroup_size", 0))}
+    return out
+
+
+def resident_workgroups(vgpr: int, lds: int, block: int) -> int:
+    """Workgroups one gfx950 compute unit holds: 4 SIMDs of 512 registers per lane (allocated in granules of 8,
+    at most 8 waves each), 160 KiB of LDS, 64-lane waves."""
+    regs = max(8, -(-vgpr // 8) * 8)
+    waves_per_simd = min(8, 512 // regs)
+    waves_per_wg = -(-block // 64)
+    by_waves = (4 * waves_per_simd) // waves_per_wg
+    by_lds = 163840 // lds if lds else by_waves
+    return min(by_waves, by_lds)
+
+
+def grid_report(trace_db: str, asm_path: str, out_md: str, cus: int = 256) -> None:
+    """Grid of every attention dispatch in start order, against the resident workgroups of that kernel."""
+    import subprocess
+
+    res = kernel_resources(asm_path)
+    demangle = {}
+    try:
+        names = list(res)
+        r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True)
+        demangle = dict(zip(r.stdout.splitlines(), names))
+    except OSError:  # pragma: no cover
+        pass
+    c = sqlite3.connect(trace_db)
+    rows = c.execute("select name, grid_x, grid_y, grid_z, workgroup_x, workgroup_y, workgroup_z, lds_size "
+                     "from kernels order by start").fetchall()
+    lines = ["| # | kernel | workgroups | threads | VGPRs (build) | LDS bytes | resident per CU | x CUs | "
+             "grid = slots |", "|---|---|---|---|---|---|---|---|---|"]
+    seen, i = set(), 0
+    for name, gx, gy, gz, wx, wy, wz, lds in rows:
+        if not family(name):
+            continue
+        wgs = (gx // wx) * (gy // wy) * (gz // wz)
+        key = (name, wgs)
+        if key in seen:
+            continue
+        seen.add(key)
+        i += 1
+        m = res.get(demangle.get(name.strip(), ""), None)
+        persistent = short_name(name).split("<")[0] in ("fwd32_kernel", "dq32_kernel", "dkv32_kernel")
+        if m:
+            per = resident_workgroups(m["vgpr"], m["lds"], m["block"])
+            slots = per * cus
+            check = ("yes" if wgs == slots else f"no ({wgs} < {slots}: fewer items)" if wgs < slots else "NO") \
+                if persistent else "not persistent"
+            lines.append(f"| {i} | `{short_name(name)}` | {wgs} | {wx * wy * wz} | {m['vgpr']} | {m['lds']} | {per} | "
+                         f"{slots} | {check} |")
+        else:
+            lines.append(f"| {i} | `{short_name(name)}` | {wgs} | {wx * wy * wz} | ? | {lds} | ? | ? | ? |")
+    head = ["# Persistent grids in one process: long-context (hd 128) kernels, then GPT-2-medium (hd 64) ones",
+            "",
+            "Commands (from the repository root on an MI355X, after `cd /tmp && export TMPDIR=/tmp`, paths "
+            "absolute, $OUT a scratch directory):", "",
+            "    rocprofv3 --kernel-trace --stats -d $OUT/prof_grid -o grid -- python3 bench.py --counters "
+            "--workloads C4,C3",
+            "    hipcc -O3 -std=c++17 --offload-arch=gfx950 -Xclang -target-feature -Xclang -packed-fp32-ops "
+            "--cuda-device-only -S exact_attention_forward_amd/csrc/fa_inst_bf16.hip -o $OUT/bf16.s",
+            "    python -m exact_attention_forward_amd.profile grid $OUT/prof_grid/grid_results.db $OUT/bf16.s "
+            "<this file>", "",
+            "The counter run steps B4 H16 T8192 hd128 (split operands) and then B64 H16 T1024 hd64 (bf16 operands), "
+            "forward and backward, in one process.  Each distinct dispatch is listed once, in order.  "
+            "`resident per CU` is what the kernel's own resources allow on gfx950 (registers and LDS from the "
+            "build's code-object metadata; 4 SIMDs of 512 registers per lane, at most 8 waves each, 160 KiB LDS); "
+            "a persistent kernel's grid must equal that times the 256 CUs (or the item count, if smaller).", ""]
+    Path(out_md).write_text("\n".join(head + lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("what", choices=("trace", "traffic", "util", "report", "lab", "configs", "traffic_all", "clock",
-                                     "split", "util_all"))
+                                     "split", "util_all", "grid"))
     ap.add_argument("db", nargs="+")
     a = ap.parse_args(argv)
     if a.what == "trace":
@@ -631,6 +715,8 @@ def main(argv=None) -> int:
         split_report(*a.db[:2])
     elif a.what == "util_all":
         util_all_report(*a.db[:2])
+    elif a.what == "grid":
+        grid_report(*a.db[:3])
     else:
         report(*a.db[:6], trace_log=a.db[6] if len(a.db) > 6 else None)
     return 0
