@@ -24,6 +24,7 @@ FA_ERR_ALIGN = -2
 FA_ERR_UNSUPPORTED = -3
 FA_ERR_ALIAS = -4
 FA_ERR_LAUNCH = -5
+FA_ERR_TOO_LARGE = -6
 
 # Every symbol include/fa.h declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -32,6 +33,7 @@ _F = ctypes.c_float
 SIGNATURES = {
     "fa_forward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_backward_nows": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_backward_delta": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_backward_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_backward_dkv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
@@ -123,6 +125,11 @@ def fa_forward_nomax(q, k, v, o, lse, B, H, T, hd, scale, causal, dtype, stream)
 def fa_backward(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, T, hd, scale, causal, dtype, prec, stream) -> int:
     return lib().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
                              _ptr(delta), B, H, T, hd, scale, int(causal), dtype, prec, _stream(stream))
+
+
+def fa_backward_nows(q, k, v, o, lse, dO, dq, dk, dv, B, H, T, hd, scale, causal, dtype, prec, stream) -> int:
+    return lib().fa_backward_nows(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), B, H, T, hd, scale, int(causal), dtype, prec, _stream(stream))
 
 
 def fa_backward_delta(o, dO, delta, B, H, T, hd, dtype, stream) -> int:

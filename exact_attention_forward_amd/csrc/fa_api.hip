@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/fa.h.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_launch.hpp"
@@ -82,6 +83,53 @@ int run(int stage, int hd, int dtype, int prec, bool causal, const void* args, v
 
 float log2e_scaled(float scale) { return (float)((double)scale * 1.4426950408889634); }
 
+// Rows of D that fa_backward_nows keeps in the library's static device array.
+constexpr size_t kScratchRows = size_t(1) << 22;
+
+}  // namespace
+
+// The D workspace of fa_backward_nows: one copy per device (each GPU the
+// library runs on holds its own), for the life of the process.  In host code
+// this name is only a stand-in for the symbol: the device address comes from
+// hipGetSymbolAddress, per device (scratch_on).
+static __device__ __align__(256) float scratch[kScratchRows];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float* scratch_addr[kMaxDevices];  // device address of `scratch`, per device id
+
+// Device address of `scratch` on device `dev`, looked up once per device with
+// that device current.  nullptr if the runtime cannot provide it.
+float* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return nullptr;
+    scratch_addr[dev] = static_cast<float*>(p);
+  }
+  return scratch_addr[dev];
+}
+
+// The device a stream launches on: the stream's own device, or the current
+// device for the null stream.
+int stream_device(void* stream, int* dev) {
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &d) != hipSuccess) return FA_ERR_LAUNCH;
+    *dev = d;
+    return FA_OK;
+  }
+  return hipGetDevice(dev) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,6 +144,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype or precision";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_TOO_LARGE: return "problem larger than the library's static workspace";
     default: return "unknown status";
   }
 }
@@ -281,6 +330,28 @@ int fa_backward(const void* q, const void* k, const void* v, const float* o, con
   if ((st = fa_backward_dq_delta(q, k, v, o, lse, dO, dq, delta, B, H, T, hd, scale, causal, dtype, prec, stream)))
     return st;
   return fa_backward_dkv(q, k, v, lse, dO, delta, dk, dv, B, H, T, hd, scale, causal, dtype, prec, stream);
+}
+
+int fa_backward_nows(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dO,
+                     float* dq, float* dk, float* dv, int B, int H, int T, int hd, float scale, int causal,
+                     fa_dtype dtype, fa_precision prec, void* stream) {
+  int st = check_common(B, H, T, hd, dtype, prec);
+  if (st) return st;
+  if ((st = check_scale(scale, causal))) return st;
+  const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv};
+  if ((st = check_ptrs(ptrs, 9))) return st;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2, nr = (size_t)B * H * T * 4;
+  const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}, {o, n * 4}, {lse, nr}, {dO, n * es}};
+  const Buf out[] = {{dq, n * 4}, {dk, n * 4}, {dv, n * 4}};
+  if ((st = check_alias(in, 6, out, 3))) return st;
+  if ((size_t)B * H * T > kScratchRows) return FA_ERR_TOO_LARGE;
+  int dev = -1;
+  if ((st = stream_device(stream, &dev))) return st;
+  float* delta = scratch_on(dev);
+  if (delta == nullptr) return FA_ERR_LAUNCH;
+  // D needs no clearing: the dQ stage writes every row of it before the
+  // dK/dV stage reads it.
+  return fa_backward(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, T, hd, scale, causal, dtype, prec, stream);
 }
 
 }  // extern "C"

@@ -63,7 +63,8 @@ enum {
   FA_ERR_ALIGN = -2,       /* a pointer is not 16-byte aligned */
   FA_ERR_UNSUPPORTED = -3, /* (hd, dtype, precision) not built */
   FA_ERR_ALIAS = -4,       /* an output overlaps an input or another output */
-  FA_ERR_LAUNCH = -5       /* the runtime rejected a kernel launch */
+  FA_ERR_LAUNCH = -5,      /* the runtime rejected a kernel launch */
+  FA_ERR_TOO_LARGE = -6    /* larger than fa_backward_nows's static workspace */
 };
 
 /*
@@ -200,6 +201,24 @@ int fa_backward_dq_delta(const void* q, const void* k, const void* v, const floa
 int fa_backward_dkv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
                     const float* delta, float* dk, float* dv, int B, int H, int T, int hd, float scale,
                     int causal, fa_dtype dtype, fa_precision prec, void* stream);
+
+/*
+ * fa_backward without the delta workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Neither this call nor anything it runs
+ * allocates or frees memory.  D lives in a static device array of the library
+ * (4,194,304 floats = 16 MiB, one copy on each GPU the library runs on, held
+ * until the process ends): B * H * T must be <= 4194304, else the call returns
+ * FA_ERR_TOO_LARGE before launching anything.  The array keeps the last
+ * call's D; nothing in it needs clearing (every row is written before it is
+ * read).  Calls that overlap in time on one GPU share the array and race:
+ * serialise them (one stream, or events).  The array's device address is
+ * looked up once per device, on the first call that runs there.  Other
+ * arguments, results and errors as fa_backward.
+ */
+int fa_backward_nows(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dO,
+                     float* dq, float* dk, float* dv, int B, int H, int T, int hd, float scale, int causal,
+                     fa_dtype dtype, fa_precision prec, void* stream);
 
 /* 1 if (hd, dtype) is built (f32: hd in {8,16,32,64,128}; bf16 and f16: {64,128}), else 0. */
 int fa_is_supported(int hd, fa_dtype dtype);

@@ -185,3 +185,20 @@ def test_half_inputs_validate(lib):
     assert fa.fa_forward_nomax(P[0], P[1], P[2], P[3], P[4], 1, 2, 8, 64, 0.1, 0, fa.FA_BF16, None) == \
         fa.FA_ERR_UNSUPPORTED
     assert fa.fa_forward_nomax(P[0], P[1], P[2], P[3], None, 1, 2, 8, 64, 0.1, 0, fa.FA_F16, None) == fa.FA_ERR_ARG
+
+
+def test_static_workspace_backward_validates(lib):
+    def nows(**kw):
+        a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], dO=P[5], dq=P[6], dk=P[7], dv=P[8], B=1, H=2, T=8,
+                 hd=64, scale=0.125, causal=1, dtype=fa.FA_F32, prec=0, stream=None)
+        a.update(kw)
+        return fa.fa_backward_nows(*a.values())
+
+    assert nows(dq=None) == fa.FA_ERR_ARG
+    assert nows(scale=0.0) == fa.FA_ERR_ARG
+    assert nows(hd=48) == fa.FA_ERR_UNSUPPORTED
+    assert nows(dv=P[8] + 4) == fa.FA_ERR_ALIGN
+    assert nows(dk=P[1]) == fa.FA_ERR_ALIAS
+    # 2^22 + 1 rows of D do not fit the static workspace (8-wide float32 rows keep the fake buffers apart)
+    assert nows(B=1, H=1, T=(1 << 22) + 1, hd=8) == fa.FA_ERR_TOO_LARGE
+    assert fa.fa_status_string(fa.FA_ERR_TOO_LARGE) == "problem larger than the library's static workspace"
