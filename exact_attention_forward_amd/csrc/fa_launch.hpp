@@ -10,6 +10,7 @@
 #include "fa_bwd32.hpp"
 #include "fa_fwd.hpp"
 #include "fa_fwd32.hpp"
+#include "fa_fwd64.hpp"
 #include "fa_split.hpp"
 #include "fa_unfused.hpp"
 
@@ -145,6 +146,14 @@ template <typename TIn, int HD, bool CAUSAL, int PREC, int CONTROL = kCtlNone>
 int run_fwd(const FwdArgs& a, hipStream_t s) {
   if constexpr (CONTROL != kCtlNone && is_bf16<TIn>) {
     return kErrUnsupported;  // the control variants are built for float32 and half inputs only
+  } else if constexpr (CONTROL == kCtlNone && is_16bit<TIn> && HD == 64) {
+    // hd 64: the pipelined forward with K/V streamed into an LDS ring
+    auto* k = &fwd64_kernel<TIn, CAUSAL, PREC>;
+    const long items = (long)((a.T + 127) / 128) * a.B * a.H;
+    FwdArgs b = a;
+    if constexpr (!is_bf16<TIn>) b.one2 = 0x3C003C00u;  // half pair (1, 1) for the row sums
+    hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, 128, items)), dim3(128), 0, s, b);
+    return launch_status();
   } else if constexpr (CONTROL == kCtlNone && is_16bit<TIn>) {
     using C = TileCfg32<HD>;
     auto* k = &fwd32_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC, C::FWD_MS>;
