@@ -28,41 +28,9 @@
 #include <type_traits>
 
 #include "fa_fwd32.hpp"
+#include "fa_ring.hpp"
 
 namespace fa {
-
-// Granule slot of column granule c in LDS row r of a 128-byte-row tile:
-// c ^ swz128(r).  Rows 0..7 map to 0, 2, 4, 6, 1, 3, 5, 7: eight consecutive
-// rows reading one granule hit eight slots, and four consecutive rows reading
-// two adjacent granules (the transposing reads) hit eight slots too.
-__device__ __forceinline__ int swz128(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// One 16-byte global-to-LDS copy per lane: lane i writes LDS bytes
-// [dst + 16 i, dst + 16 i + 16), dst uniform across the wave.  Issued as
-// inline assembly so that the compiler does not track it (it would drain every
-// outstanding copy before LDS reads it cannot prove disjoint from them);
-// callers wait for completion explicitly.
-__device__ __forceinline__ void lds_copy16(const void* src, unsigned dst) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory", "m0");
-}
-// The same copy from a wave-uniform base address plus a per-lane 32-bit byte
-// offset (no per-lane 64-bit address arithmetic).
-__device__ __forceinline__ void lds_copy16(const void* base, unsigned off, unsigned dst) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(dst)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(n) for n in 0..15 (the other counters unconstrained).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-  }
-}
 
 template <typename TIn, bool CAUSAL, int PREC>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd64_kernel(FwdArgs a) {

@@ -8,6 +8,7 @@
 
 #include "fa_bwd.hpp"
 #include "fa_bwd32.hpp"
+#include "fa_bwd64.hpp"
 #include "fa_fwd.hpp"
 #include "fa_fwd32.hpp"
 #include "fa_fwd64.hpp"
@@ -218,7 +219,13 @@ int run_dkv(const BwdArgs& a, hipStream_t s) {
   // 16-bit hd 128 runs the 16x16 kernel: 32 keys x 128 columns of dK and dV
   // per wave hold the 32x32 kernel to one wave per SIMD (502 VGPRs), and the
   // 16x16 one at two waves per SIMD is 12-13% faster at B4 H16 T8192.
-  if constexpr (is_16bit<TIn> && HD <= 64) {
+  if constexpr (is_16bit<TIn> && HD == 64) {
+    // hd 64: Q/dO blocks and the K/V tiles streamed through an LDS ring
+    auto* k = &dkv64_kernel<TIn, CAUSAL, PREC>;
+    const long items = (long)((a.T + 127) / 128) * a.B * a.H;
+    hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, 256, items)), dim3(256), 0, s, a);
+    return launch_status();
+  } else if constexpr (is_16bit<TIn> && HD <= 64) {
     using C = TileCfg32<HD>;
     auto* k = &dkv32_kernel<TIn, HD, CAUSAL, PREC, C::DKV_NW, C::DKV_BQ>;
     const long items = (long)((a.T + C::DKV_NW * 32 - 1) / (C::DKV_NW * 32)) * a.B * a.H;
