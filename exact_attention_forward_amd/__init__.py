@@ -9,7 +9,7 @@ provides memory and streams) and the seeded input generators (``inputs``).
 from ._binding import (FA_BF16, FA_F16, FA_ERR_ALIAS, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_LAUNCH, FA_ERR_TOO_LARGE, FA_ERR_UNSUPPORTED, FA_F32,
                        FA_OK, FA_PREC_BF16, FA_PREC_BF16X2, FA_PREC_DEFAULT, FaError, check, fa_backward,
                        fa_backward_delta, fa_backward_dkv, fa_backward_nows, fa_backward_dq, fa_backward_dq_delta, fa_forward,
-                       fa_forward_nomax, fa_forward_norescale, fa_forward_splitkv, fa_forward_unfused, fa_is_supported, fa_status_string, lib, library_path)
+                       fa_forward_auto_splits, fa_forward_nomax, fa_forward_norescale, fa_forward_splitkv, fa_forward_unfused, fa_is_supported, fa_status_string, lib, library_path)
 
 
 def __getattr__(name):

@@ -39,6 +39,7 @@ SIGNATURES = {
     "fa_backward_dkv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_backward_dq_delta": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_forward_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
+    "fa_forward_auto_splits": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "fa_forward_unfused": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_forward_norescale": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_forward_nomax": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
@@ -105,6 +106,10 @@ def fa_forward(q, k, v, o, lse, B, H, T, hd, scale, causal, dtype, prec, stream)
 def fa_forward_splitkv(q, k, v, o, lse, ws, B, H, T, hd, scale, causal, nsplit, dtype, prec, stream) -> int:
     return lib().fa_forward_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), B, H, T, hd, scale,
                                     int(causal), nsplit, dtype, prec, _stream(stream))
+
+
+def fa_forward_auto_splits(B, H, T, hd, causal, dtype, prec) -> int:
+    return lib().fa_forward_auto_splits(B, H, T, hd, int(causal), dtype, prec)
 
 
 def fa_forward_unfused(q, k, v, o, scores, B, H, T, hd, scale, causal, dtype, stream) -> int:

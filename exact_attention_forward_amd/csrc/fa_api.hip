@@ -161,7 +161,7 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
   const Buf out[] = {{o, n * 4}, {lse, (size_t)B * H * T * 4}};
   if ((st = check_alias(in, 3, out, 2))) return st;
   fa::FwdArgs a{q, k, v, o, lse, B, H, T, log2e_scaled(scale)};
-  return run(fa::kFwd, hd, dtype, prec, causal != 0, &a, stream);
+  return run(fa::kFwdAuto, hd, dtype, prec, causal != 0, &a, stream);
 }
 
 int fa_forward_splitkv(const void* q, const void* k, const void* v, float* o, float* lse, float* ws, int B, int H,
@@ -172,14 +172,31 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, float* o, fl
   if ((st = check_scale(scale, causal))) return st;
   if (nsplit < 1 || nsplit > 64) return FA_ERR_ARG;
   if ((double)B * H > 65535.0) return FA_ERR_ARG;
+  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2, nr = (size_t)B * H * T;
+  if (nsplit == 1 && ws == nullptr) {
+    // one range and no workspace: the plain forward, never split
+    const void* ptrs[] = {q, k, v, o, lse};
+    if ((st = check_ptrs(ptrs, 5))) return st;
+    const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}};
+    const Buf out[] = {{o, n * 4}, {lse, nr * 4}};
+    if ((st = check_alias(in, 3, out, 2))) return st;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, T, log2e_scaled(scale)};
+    return run(fa::kFwd, hd, dtype, prec, causal != 0, &a, stream);
+  }
   const void* ptrs[] = {q, k, v, o, lse, ws};
   if ((st = check_ptrs(ptrs, 6))) return st;
-  const size_t n = (size_t)B * T * H * hd, es = dtype == FA_F32 ? 4 : 2, nr = (size_t)B * H * T;
   const Buf in[] = {{q, n * es}, {k, n * es}, {v, n * es}};
   const Buf out[] = {{o, n * 4}, {lse, nr * 4}, {ws, (size_t)nsplit * (n + nr) * 4}};
   if ((st = check_alias(in, 3, out, 3))) return st;
   fa::SplitArgs a{{q, k, v, ws, ws + (size_t)nsplit * n, B, H, T, log2e_scaled(scale)}, o, lse, nsplit};
   return run(fa::kFwdSplit, hd, dtype, prec, causal != 0, &a, stream);
+}
+
+int fa_forward_auto_splits(int B, int H, int T, int hd, int causal, fa_dtype dtype, fa_precision prec) {
+  int st = check_common(B, H, T, hd, dtype, prec);
+  if (st) return st;
+  fa::FwdArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, B, H, T, 0.f};
+  return run(fa::kFwdSplits, hd, dtype, prec, causal != 0, &a, nullptr);
 }
 
 static int control_forward(int stage, const void* q, const void* k, const void* v, float* o, float* lse, int B,

@@ -282,7 +282,117 @@ int run_fwd_split(const SplitArgs& sa, hipStream_t s) {
   return launch_status();
 }
 
-enum Stage { kFwd = 0, kDq = 1, kDkv = 2, kDqDelta = 3, kFwdNoRescale = 4, kFwdSplit = 5, kFwdNoMax = 6 };
+// The plain forward's work items and the workgroups of its kernel the chip
+// holds at once.
+template <typename TIn, int HD, bool CAUSAL, int PREC>
+void fwd_fill(const FwdArgs& a, long* items, long* slots) {
+  const long bh = (long)a.B * a.H;
+  if constexpr (is_16bit<TIn> && HD == 64) {
+    *items = (long)((a.T + 127) / 128) * bh;
+    *slots = (long)resident_per_cu(reinterpret_cast<const void*>(&fwd64_kernel<TIn, CAUSAL, PREC>), 128) * device_cus();
+  } else if constexpr (is_16bit<TIn>) {
+    using C = TileCfg32<HD>;
+    constexpr int BR = C::FWD_NW * 32 * C::FWD_MS;
+    *items = (long)((a.T + BR - 1) / BR) * bh;
+    *slots = (long)resident_per_cu(
+                 reinterpret_cast<const void*>(&fwd32_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_BC, C::FWD_MS>),
+                 C::FWD_NW * 64) * device_cus();
+  } else {
+    using C = TileCfg<TIn, HD>;
+    constexpr int BR = C::FWD_NW * 16 * C::FWD_MR;
+    *items = (long)((a.T + BR - 1) / BR) * bh;
+    *slots = (long)resident_per_cu(
+                 reinterpret_cast<const void*>(&fwd_kernel<TIn, HD, CAUSAL, PREC, C::FWD_NW, C::FWD_MR, C::FWD_BC>),
+                 C::FWD_NW * 64) * device_cus();
+  }
+}
+
+// Key splits for a forward whose work items fill at most half of the resident
+// workgroups (few batch-heads, long rows): enough splits to fill them, at
+// most 64 and at least 128 keys per split; 1 otherwise.
+inline int auto_splits(long items, long slots, int T) {
+  if (items <= 0 || 2 * items > slots) return 1;
+  long n = slots / items;
+  if (n > 64) n = 64;
+  if (n > T / 128) n = T / 128;
+  return n >= 2 ? (int)n : 1;
+}
+
+// The library's workspace for stream s: one buffer per (device, stream),
+// allocated on first use, grown when a call needs more (after waiting for the
+// stream, so that no queued work still uses the old buffer) and kept until the
+// process ends.  Calls on one stream run in order, so they can share it.
+// Returns null (the caller then does without) if the stream is being captured
+// and the buffer would have to grow, or if an allocation fails.
+inline float* stream_workspace(hipStream_t s, size_t bytes) {
+  int dev = -1;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  struct Entry {
+    int dev;
+    hipStream_t s;
+    float* p;
+    size_t bytes;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  Entry* e = nullptr;
+  for (auto& x : cache)
+    if (x.dev == dev && x.s == s) e = &x;
+  if (e != nullptr && e->bytes >= bytes) return e->p;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  float* p = nullptr;
+  bool ok = true;
+  if (e != nullptr) ok = hipStreamSynchronize(s) == hipSuccess && hipFree(e->p) == hipSuccess;
+  ok = ok && hipMalloc(reinterpret_cast<void**>(&p), bytes) == hipSuccess;
+  (void)hipSetDevice(cur);
+  if (!ok) {
+    (void)hipGetLastError();
+    if (e != nullptr) {
+      e->p = nullptr;
+      e->bytes = 0;
+    }
+    return nullptr;
+  }
+  if (e == nullptr) cache.push_back(Entry{dev, s, p, bytes});
+  else {
+    e->p = p;
+    e->bytes = bytes;
+  }
+  return p;
+}
+
+// fa_forward: the plain forward, or the split-key forward with nsplit from
+// auto_splits in the stream's workspace (the plain forward without one).
+template <typename TIn, int HD, bool CAUSAL, int PREC>
+int run_fwd_auto(const FwdArgs& a, hipStream_t s) {
+  long items = 0, slots = 0;
+  fwd_fill<TIn, HD, CAUSAL, PREC>(a, &items, &slots);
+  const int nsplit = auto_splits(items, slots, a.T);
+  if (nsplit < 2) return run_fwd<TIn, HD, CAUSAL, PREC>(a, s);
+  const size_t n = (size_t)a.B * a.T * a.H * HD, nr = (size_t)a.B * a.H * a.T;
+  float* ws = stream_workspace(s, (size_t)nsplit * (n + nr) * sizeof(float));
+  if (ws == nullptr) return run_fwd<TIn, HD, CAUSAL, PREC>(a, s);
+  FwdArgs f = a;
+  f.o = ws;
+  f.lse = ws + (size_t)nsplit * n;
+  return run_fwd_split<TIn, HD, CAUSAL, PREC>(SplitArgs{f, a.o, a.lse, nsplit}, s);
+}
+
+enum Stage { kFwd = 0, kDq = 1, kDkv = 2, kDqDelta = 3, kFwdNoRescale = 4, kFwdSplit = 5, kFwdNoMax = 6, kFwdAuto = 7,
+            kFwdSplits = 8 };
 
 template <typename TIn, int HD, bool CAUSAL, int PREC>
 int run_stage(int stage, const void* args, hipStream_t s) {
@@ -291,6 +401,12 @@ int run_stage(int stage, const void* args, hipStream_t s) {
     case kFwdNoRescale: return run_fwd<TIn, HD, CAUSAL, PREC, kCtlNoRescale>(*static_cast<const FwdArgs*>(args), s);
     case kFwdNoMax: return run_fwd<TIn, HD, CAUSAL, PREC, kCtlNoMax>(*static_cast<const FwdArgs*>(args), s);
     case kFwdSplit: return run_fwd_split<TIn, HD, CAUSAL, PREC>(*static_cast<const SplitArgs*>(args), s);
+    case kFwdAuto: return run_fwd_auto<TIn, HD, CAUSAL, PREC>(*static_cast<const FwdArgs*>(args), s);
+    case kFwdSplits: {  // the split count run_fwd_auto would use (no launch)
+      long items = 0, slots = 0;
+      fwd_fill<TIn, HD, CAUSAL, PREC>(*static_cast<const FwdArgs*>(args), &items, &slots);
+      return auto_splits(items, slots, static_cast<const FwdArgs*>(args)->T);
+    }
     case kDq: return run_dq<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);
     case kDqDelta: return run_dq<TIn, HD, CAUSAL, PREC, true>(*static_cast<const BwdArgs*>(args), s);
     default: return run_dkv<TIn, HD, CAUSAL, PREC>(*static_cast<const BwdArgs*>(args), s);

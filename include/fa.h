@@ -76,6 +76,21 @@ enum {
  *   q, k, v   [B, T, H, hd] inputs of `dtype`
  *   o         [B, T, H, hd] float32 output
  *   lse       [B, H, T] float32 output
+ * When the plain forward's work items (query tiles of 128 rows, per batch and
+ * head) would fill at most half of the workgroups the GPU holds at once (few
+ * (batch, head) pairs, long rows), fa_forward runs the split-key forward of
+ * fa_forward_splitkv instead, with nsplit = min(64, resident workgroups /
+ * work items, T / 128); the results then equal the unsplit ones up to
+ * rounding, as described there.  Its workspace is one device buffer per
+ * (device, stream) that the library allocates on first use and keeps until
+ * the process ends; a call that needs a larger one waits for `stream`, frees
+ * the old buffer and allocates a new one.  If the stream is being captured
+ * into a graph and the buffer would have to grow, or an allocation fails,
+ * fa_forward runs unsplit (so capture after one call of the same size).
+ * Concurrent calls on one stream from several host threads are serialised
+ * by the stream; they share the buffer safely only because the stream runs
+ * their kernels in order.  fa_forward_splitkv with nsplit = 1 and
+ * ws = NULL always runs the plain forward and allocates nothing.
  */
 int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int T, int hd,
                float scale, int causal, fa_dtype dtype, fa_precision prec, void* stream);
@@ -92,7 +107,9 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
  * rounding (not bit for bit): float32 summation order, and for 16-bit inputs
  * the rounding of P, which each split takes against its own running max.
  *   ws      float32 workspace of nsplit * (B*T*H*hd + B*H*T) elements,
- *           caller-allocated; overwritten
+ *           caller-allocated; overwritten.  May be NULL when nsplit = 1:
+ *           then the plain forward runs (no split, no workspace, results
+ *           bit for bit those of an unsplit fa_forward)
  *   nsplit  1 .. 64
  * Other arguments and the contract as fa_forward.  Extra limit: B*H <=
  * 65535.
@@ -100,6 +117,13 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
 int fa_forward_splitkv(const void* q, const void* k, const void* v, float* o, float* lse, float* ws, int B, int H,
                        int T, int hd, float scale, int causal, int nsplit, fa_dtype dtype, fa_precision prec,
                        void* stream);
+
+/*
+ * The key-split count fa_forward uses for these sizes on the current device
+ * (1: no split), as described at fa_forward.  Returns a count >= 1, or a
+ * negative status for invalid or unsupported arguments.  Launches nothing.
+ */
+int fa_forward_auto_splits(int B, int H, int T, int hd, int causal, fa_dtype dtype, fa_precision prec);
 
 /*
  * Unfused forward (float32 inputs only), the comparator of the fused-attention

@@ -159,6 +159,17 @@ def test_unfused_and_control_entry_points_validate(lib):
         fa.FA_ERR_ALIAS
 
 
+def test_auto_splits_validates(lib):
+    # argument checks run before the device is asked anything
+    q = lambda **kw: fa.fa_forward_auto_splits(*{**dict(B=1, H=1, T=4096, hd=64, causal=1, dtype=fa.FA_BF16,
+                                                        prec=0), **kw}.values())
+    assert q(B=0) == fa.FA_ERR_ARG
+    assert q(T=0) == fa.FA_ERR_ARG
+    assert q(hd=48) == fa.FA_ERR_UNSUPPORTED
+    assert q(prec=7) == fa.FA_ERR_ARG
+    assert q(dtype=fa.FA_F32, prec=fa.FA_PREC_BF16) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_splitkv_validates(lib):
     args = lambda **kw: {**dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], ws=P[5], B=1, H=2, T=8, hd=64, scale=0.1,
                                 causal=1, nsplit=4, dtype=fa.FA_F32, prec=0, stream=None), **kw}

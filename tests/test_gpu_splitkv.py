@@ -78,3 +78,89 @@ def test_splitkv_agrees_with_fused_on_one_long_head():
     o2, l2 = run_split(c, 16)
     torch.cuda.synchronize()
     assert float((o1 - o2).abs().max()) <= 1e-5 and float((l1 - l2).abs().max()) <= 1e-5
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_auto_split(dt, causal):
+    # One head of T = 4096: the plain forward's 32 query tiles would leave most
+    # of the GPU idle, so fa_forward splits the keys.  Its result must be the
+    # split-key forward's for the count it reports, bit for bit, and meet the
+    # oracle bar.
+    B, H, T, hd = 1, 1, 4096, 64
+    c = I.make_case("auto_split", B, H, T, hd, I.BF16 if dt == "bf16" else I.F32, causal, 77)
+    fdt = fa.FA_BF16 if dt == "bf16" else fa.FA_F32
+    n = fa.fa_forward_auto_splits(B, H, T, hd, int(causal), fdt, fa.FA_PREC_DEFAULT)
+    print(f"[auto split] {dt} causal={causal} nsplit={n}", flush=True)
+    assert 2 <= n <= 64
+    q, k, v = (to_device(c, x) for x in ("q", "k", "v"))
+    o = torch.full((B, T, H, hd), float("nan"), device="cuda")
+    lse = torch.full((B, H, T), float("nan"), device="cuda")
+    fa.check(fa.fa_forward(q, k, v, o, lse, B, H, T, hd, c.scale, int(causal), fdt, fa.FA_PREC_DEFAULT, None))
+    o2, l2 = run_split(c, n)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+    err = oracle_errors(c, o, lse)
+    tol = BF16_TOL if dt == "bf16" else F32_TOL
+    assert err["O"] <= tol and err["L"] <= tol, err
+
+
+def test_forward_auto_split_leaves_full_workloads_alone():
+    # 8192 query tiles at B64 H16 T1024 fill the GPU: no split
+    assert fa.fa_forward_auto_splits(64, 16, 1024, 64, 1, fa.FA_BF16, fa.FA_PREC_DEFAULT) == 1
+    assert fa.fa_forward_auto_splits(4, 16, 8192, 128, 1, fa.FA_BF16, fa.FA_PREC_BF16X2) == 1
+
+
+def test_splitkv_without_workspace_is_the_plain_forward():
+    # nsplit = 1 and no workspace: the plain forward, bit for bit the unsplit
+    # fa_forward of a workload it does not split, and within the oracle bar for
+    # one it would split
+    c = I.make_case("plain", 8, 16, 1024, 64, I.BF16, True, 5)
+    assert fa.fa_forward_auto_splits(8, 16, 1024, 64, 1, fa.FA_BF16, fa.FA_PREC_DEFAULT) == 1
+    q, k, v = (to_device(c, x) for x in ("q", "k", "v"))
+    o1, l1 = torch.empty(q.shape, device="cuda"), torch.empty((8, 16, 1024), device="cuda")
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    fa.check(fa.fa_forward(q, k, v, o1, l1, 8, 16, 1024, 64, c.scale, 1, fa.FA_BF16, 0, None))
+    fa.check(fa.fa_forward_splitkv(q, k, v, o2, l2, None, 8, 16, 1024, 64, c.scale, 1, 1, fa.FA_BF16, 0, None))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    c1 = I.make_case("plain_one_head", 1, 1, 2048, 64, I.BF16, True, 6)
+    q, k, v = (to_device(c1, x) for x in ("q", "k", "v"))
+    o = torch.full((1, 2048, 1, 64), float("nan"), device="cuda")
+    lse = torch.full((1, 1, 2048), float("nan"), device="cuda")
+    fa.check(fa.fa_forward_splitkv(q, k, v, o, lse, None, 1, 1, 2048, 64, c1.scale, 1, 1, fa.FA_BF16, 0, None))
+    torch.cuda.synchronize()
+    err = oracle_errors(c1, o, lse)
+    assert err["O"] <= BF16_TOL and err["L"] <= BF16_TOL, err
+
+
+def test_forward_auto_split_under_graph_capture():
+    # A capture on a stream without a workspace yet cannot allocate one: the
+    # captured fa_forward is the plain forward.  After one call on the stream
+    # the workspace exists and the captured call splits.  Each graph is
+    # replayed three times, with eager work between replays.
+    B, H, T, hd = 1, 1, 2048, 64
+    c = I.make_case("auto_split_graph", B, H, T, hd, I.BF16, True, 91)
+    n = fa.fa_forward_auto_splits(B, H, T, hd, 1, fa.FA_BF16, fa.FA_PREC_DEFAULT)
+    assert n >= 2
+    q, k, v = (to_device(c, x) for x in ("q", "k", "v"))
+    po, pl = torch.empty((B, T, H, hd), device="cuda"), torch.empty((B, H, T), device="cuda")
+    fa.check(fa.fa_forward_splitkv(q, k, v, po, pl, None, B, H, T, hd, c.scale, 1, 1, fa.FA_BF16, 0, None))
+    so, sl = run_split(c, n)
+    for warm in (False, True):
+        s = torch.cuda.Stream()
+        o = torch.full((B, T, H, hd), float("nan"), device="cuda")
+        lse = torch.full((B, H, T), float("nan"), device="cuda")
+        if warm:
+            fa.check(fa.fa_forward(q, k, v, o, lse, B, H, T, hd, c.scale, 1, fa.FA_BF16, 0, s))
+            s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fa.check(fa.fa_forward(q, k, v, o, lse, B, H, T, hd, c.scale, 1, fa.FA_BF16, 0, s))
+        eo, el = (so, sl) if warm else (po, pl)
+        for _ in range(3):
+            o.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, eo) and torch.equal(lse, el), f"warm={warm}"
