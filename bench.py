@@ -70,7 +70,7 @@ METRIC = "attention fwd+bwd TFLOP/s (% MFMA peak), causal B64 H16 T1024 hd64, 1 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 STAGES = ("fwd", "dq", "dkv")
-KERNEL_NAMES = {"fwd": "fwd32_kernel", "dq": "dq32_kernel", "dkv": "dkv32_kernel"}
+KERNEL_NAMES = {"fwd": "fwd64_kernel", "dq": "dq32_kernel", "dkv": "dkv64_kernel"}
 COPY_BYTES = 1 << 30
 
 
@@ -276,6 +276,9 @@ def lab(args) -> int:
             ws = torch.empty((nsplit * (N * d + N),), device=dev)
             runs = {
                 "fused": lambda: fa.check(fa.fa_forward(q, k, v, o, lse, 1, 1, N, d, c.scale, 0, fa.FA_F32, 0, stream)),
+                # the plain fused kernel: no key split (fa_forward splits by itself here)
+                "plain": lambda: fa.check(fa.fa_forward_splitkv(q, k, v, o, lse, None, 1, 1, N, d, c.scale, 0, 1,
+                                                                fa.FA_F32, 0, stream)),
                 "unfused": lambda: fa.check(fa.fa_forward_unfused(q, k, v, o, s, 1, 1, N, d, c.scale, 0, fa.FA_F32,
                                                                   stream)),
                 "broken": lambda: fa.check(fa.fa_forward_norescale(q, k, v, o, lse, 1, 1, N, d, c.scale, 0, fa.FA_F32,
@@ -283,7 +286,8 @@ def lab(args) -> int:
                 "split": lambda: fa.check(fa.fa_forward_splitkv(q, k, v, o, lse, ws, 1, 1, N, d, c.scale, 0, nsplit,
                                                                 fa.FA_F32, 0, stream)),
             }
-            row = {"N": N, "d": d, "nsplit": nsplit}
+            row = {"N": N, "d": d, "nsplit": nsplit,
+                   "auto_nsplit": fa.fa_forward_auto_splits(1, 1, N, d, 0, fa.FA_F32, 0)}
             for kind, fn in runs.items():
                 if args.counters:
                     fn()
@@ -302,6 +306,7 @@ def lab(args) -> int:
                 row[kind + "_ms"] = round(sorted(ts)[len(ts) // 2], 5)
             if not args.counters:
                 row["unfused_over_fused"] = round(row["unfused_ms"] / row["fused_ms"], 3)
+                row["unfused_over_plain"] = round(row["unfused_ms"] / row["plain_ms"], 3)
                 row["unfused_over_split"] = round(row["unfused_ms"] / row["split_ms"], 3)
                 row["score_bytes_saved"] = 16 * N * N
             rows.append(row)

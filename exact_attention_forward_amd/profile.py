@@ -41,8 +41,18 @@ import sys
 from pathlib import Path
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-ATTN_KERNELS = ("fwd32_kernel", "dq32_kernel", "dkv32_kernel", "fwd_kernel", "dq_kernel", "dkv_kernel",
-                "delta_kernel")
+ATTN_KERNELS = ("fwd64_kernel", "dkv64_kernel", "fwd32_kernel", "dq32_kernel", "dkv32_kernel", "fwd_kernel",
+                "dq_kernel", "dkv_kernel", "delta_kernel")
+# the kernels of the bench workload (B64 H16 T1024 hd64 bf16), forward, dQ, dK/dV
+BENCH_KERNELS = ("fwd64_kernel", "dq32_kernel", "dkv64_kernel")
+
+
+def stage_of(fam: str) -> str:
+    """'fwd', 'dq', 'dkv' or 'delta' for a kernel family name."""
+    for st in ("fwd", "dkv", "dq", "delta"):
+        if fam.startswith(st):
+            return st
+    raise KeyError(fam)
 
 
 def short_name(k: str) -> str:
@@ -176,7 +186,7 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
 
     # compulsory bytes per launch: every tensor once (bf16 inputs, f32 O / L / D / grads; D fused into dQ)
     comp = {fam: compulsory_bytes(fam, B, H, T, hd, 2, fused_d=True)
-            for fam in ("fwd32_kernel", "dq32_kernel", "dkv32_kernel")}
+            for fam in BENCH_KERNELS}
     fr = fused_requests(T, hd, fwd_rows, True)
     fr_nc = fused_requests(T, hd, fwd_rows, False)
     lines = [f"# HBM traffic per launch: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
@@ -189,7 +199,7 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
              f"way, so reads are scaled by {tr['read_scale']:.4f} and writes by {tr['write_scale']:.4f}.", "",
              "| kernel | avg us | HBM read MB | HBM write MB | HBM GB/s | % of 8 TB/s | read / compulsory | write / compulsory |",
              "|---|---|---|---|---|---|---|---|"]
-    for fam in ("fwd32_kernel", "dq32_kernel", "dkv32_kernel"):
+    for fam in BENCH_KERNELS:
         if fam not in tr["kernels"]:
             continue
         k = tr["kernels"][fam]
@@ -198,7 +208,7 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
         cr, cw = comp[fam]
         lines.append(f"| `{k['kernel']}` | {t_us:.1f} | {k['hbm_read_bytes'] / 1e6:.1f} | {k['hbm_write_bytes'] / 1e6:.1f} "
                      f"| {gbs:.0f} | {100 * gbs / 8000:.1f} | {k['hbm_read_bytes'] / cr:.2f} | {k['hbm_write_bytes'] / cw:.2f} |")
-    fwd = tr["kernels"].get("fwd32_kernel")
+    fwd = tr["kernels"].get(BENCH_KERNELS[0])
     lines += ["", "Forward against the closed form of the fused-attention facts page (block `traffic`), per head, "
               f"N = {T}, d = {hd}, query tiles of {fwd_rows} rows (G = {fr['G']}), counted in elements:", "",
               f"* page form, no mask: reads N d + 2 G N d = {fr_nc['reads']}, writes N d = {fr_nc['writes']};",
@@ -225,7 +235,7 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
                   ", ".join(f"`{k}` {1e3 * v['ms']:.1f} us" for k, v in bk.items()) + "."]
     (out / "kernel_trace_gpt2m_bf16.md").write_text("\n".join(lines) + "\n")
 
-    flops = {"fwd32_kernel": 4, "dq32_kernel": 6, "dkv32_kernel": 8}
+    flops = {"fwd": 4, "dq": 6, "dkv": 8}
     pairs = heads * T * T / 2
     lines = [f"# Matrix-core and vector-ALU use: causal attention fwd+bwd, B{B} H{H} T{T} hd{hd}, bf16 (MI355X)", "",
              "Command (from the repository root on an MI355X, after `cd /tmp && export TMPDIR=/tmp`, paths absolute, $OUT a scratch directory):", "",
@@ -236,12 +246,12 @@ def report(trace_db, fetch_db, write_db, util_db, out_dir, src_hash,
              "(forward 4 hd, dQ kernel 6 hd, dK/dV kernel 8 hd; B H T^2 / 2 pairs).", "",
              "| kernel | avg us | MfmaUtil % | VALUBusy % | LDSBankConflict % | OccupancyPercent % | executed GFLOP | "
              "algorithmic GFLOP | algorithmic TFLOP/s |", "|---|---|---|---|---|---|---|---|---|"]
-    for fam in ("fwd32_kernel", "dq32_kernel", "dkv32_kernel"):
+    for fam in BENCH_KERNELS:
         if fam not in ut:
             continue
         u = ut[fam]
         t_us = avg_us.get(fam, float("nan"))
-        alg = flops[fam] * hd * pairs
+        alg = flops[stage_of(fam)] * hd * pairs
         lines.append(f"| `{u['kernel']}` | {t_us:.1f} | {u.get('MfmaUtil', float('nan')):.1f} | "
                      f"{u.get('VALUBusy', float('nan')):.1f} | {u.get('LDSBankConflict', float('nan')):.1f} | "
                      f"{u.get('OccupancyPercent', float('nan')):.1f} | "
@@ -266,10 +276,11 @@ def dispatch_counter(db: str, cn: str) -> list:
 def lab_bytes(fetch_db: str, write_db: str) -> dict:
     """(N, d, kind) -> (read bytes, write bytes) from a ``bench.py --lab --counters`` run.
 
-    That run launches, for d in (16, 64) and N in (256, ..., 4096): the fused
-    forward (one kernel), the unfused forward (scores, softmax, P V), the
-    no-rescale control (one kernel) and the split-key forward (partials,
-    merge), in this order.
+    That run launches, for d in (16, 64) and N in (256, ..., 4096): fa_forward
+    (one kernel, or partials and merge when it splits the keys by itself), the
+    plain fused kernel (one kernel), the unfused forward (scores, softmax,
+    P V), the no-rescale control (one kernel) and the split-key forward
+    (partials, merge), in this order.
     """
     f, w = dispatch_counter(fetch_db, "FETCH_SIZE"), dispatch_counter(write_db, "WRITE_SIZE")
     rscale = (1 << 30) / 1024 / max(v for k, v in f if COPY_KERNEL in k)
@@ -279,7 +290,9 @@ def lab_bytes(fetch_db: str, write_db: str) -> dict:
     out, i = {}, 0
     for d in LAB_WIDTHS:
         for N in LAB_SIZES:
-            for kind, nk in (("fused", 1), ("unfused", 3), ("broken", 1), ("split", 2)):
+            for kind, nk in (("fused", 1), ("plain", 1), ("unfused", 3), ("broken", 1), ("split", 2)):
+                if kind == "fused" and i + 1 < len(fk) and "merge_kernel" in fk[i + 1][0]:
+                    nk = 2
                 r = sum(v for _, v in fk[i:i + nk]) * 1024 * rscale
                 wr = sum(v for _, v in wk[i:i + nk]) * 1024 * wscale
                 out[(N, d, kind)] = (r, wr)
@@ -305,25 +318,31 @@ def lab_report(lab_log: str, fetch_db: str, write_db: str, out_md: str) -> None:
              "(HIP events; the unfused forward's three kernels in one timed run).  Bytes: FETCH_SIZE and WRITE_SIZE "
              "per run, scaled by a 1 GiB device copy as in the other summaries.  Every kind is checked against the "
              "float64 reference with the lesson's error bound by tests/test_gpu_lab.py (fused and unfused pass, the "
-             "no-rescale control fails).  The lesson predicts that the fused kernel saves exactly 16 N^2 bytes: the "
-             "score matrix written, read, written as P and read again.", "",
-             "| N | d | fused ms | unfused ms | no-rescale ms | split-key ms (splits) | unfused / fused | "
-             "unfused / split | fused MB | unfused MB | saved MB | predicted 16 N^2 MB | saved / predicted |",
-             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "no-rescale control fails).  Kinds: `fa_forward` as a caller gets it (it splits the keys by itself "
+             "when one head cannot fill the GPU; its split count in brackets), the plain fused kernel (one "
+             "workgroup per 128 query rows, fa_forward_splitkv with nsplit = 1 and no workspace), the unfused "
+             "forward, the no-rescale control and fa_forward_splitkv at 128 keys per split.  The lesson predicts "
+             "that the plain fused kernel saves exactly 16 N^2 bytes against the unfused one: the score matrix "
+             "written, read, written as P and read again.", "",
+             "| N | d | fa_forward ms (splits) | plain fused ms | unfused ms | no-rescale ms | split-key ms (splits) | "
+             "unfused / fa_forward | unfused / plain | plain MB | unfused MB | saved MB | predicted 16 N^2 MB | "
+             "saved / predicted |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in (rec or {}).get("rows", []):
         N, d = r["N"], r["d"]
-        fb = sum(by[(N, d, "fused")])
+        fb = sum(by[(N, d, "plain")])
         ub = sum(by[(N, d, "unfused")])
         pred = 16 * N * N
-        lines.append(f"| {N} | {d} | {r['fused_ms']:.4f} | {r['unfused_ms']:.4f} | {r['broken_ms']:.4f} | "
-                     f"{r['split_ms']:.4f} ({r['nsplit']}) | {r['unfused_over_fused']:.2f} | "
-                     f"{r['unfused_over_split']:.2f} | {fb / 1e6:.2f} | {ub / 1e6:.2f} | {(ub - fb) / 1e6:.2f} | "
-                     f"{pred / 1e6:.2f} | {(ub - fb) / pred:.2f} |")
-    lines += ["", "One head gives the fused kernel only ceil(N / 128) workgroups (32 at N = 4096) on 256 compute "
-              "units, while the unfused kernels spread N^2 / 4096 score tiles over the chip; the time is set by that "
-              "parallelism (and, at d = 16, by the score traffic), not by global memory alone.  The split-key "
-              "forward (fa_forward_splitkv) keeps the fused kernel's traffic but runs (N / 128)^2 workgroups and "
-              "merges their partial (O, L) states."]
+        lines.append(f"| {N} | {d} | {r['fused_ms']:.4f} ({r['auto_nsplit']}) | {r['plain_ms']:.4f} | "
+                     f"{r['unfused_ms']:.4f} | {r['broken_ms']:.4f} | {r['split_ms']:.4f} ({r['nsplit']}) | "
+                     f"{r['unfused_over_fused']:.2f} | {r['unfused_over_plain']:.2f} | {fb / 1e6:.2f} | "
+                     f"{ub / 1e6:.2f} | {(ub - fb) / 1e6:.2f} | {pred / 1e6:.2f} | {(ub - fb) / pred:.2f} |")
+    lines += ["", "One head gives the plain fused kernel only ceil(N / 128) workgroups (32 at N = 4096) on 256 "
+              "compute units, while the unfused kernels spread N^2 / 4096 score tiles over the chip; the plain "
+              "kernel's time is set by that parallelism (and, at d = 16, by the score traffic), not by global "
+              "memory alone.  fa_forward therefore splits the keys when its work items fill at most half of the "
+              "resident workgroups: it keeps the fused kernel's freedom from the score matrix, adds the partial "
+              "(O, L) states and their merge, and runs (N / 128) x splits workgroups."]
     Path(out_md).write_text("\n".join(lines) + "\n")
 
 
@@ -364,17 +383,16 @@ def compulsory_bytes(fam: str, B: int, H: int, T: int, hd: int, e: int, fused_d:
     dO, L and D and writes dK and dV.  The D pre-pass reads O and dO and writes D.
     """
     n, r = B * H * T * hd, B * H * T
-    if fam in ("fwd32_kernel", "fwd_kernel"):
+    st = stage_of(fam)
+    if st == "fwd":
         return 3 * n * e, 4 * n + 4 * r
-    if fam in ("dq32_kernel", "dq_kernel"):
+    if st == "dq":
         if fused_d:
             return 4 * n * e + 4 * n + 4 * r, 4 * n + 4 * r
         return 4 * n * e + 8 * r, 4 * n
-    if fam in ("dkv32_kernel", "dkv_kernel"):
+    if st == "dkv":
         return 4 * n * e + 8 * r, 8 * n
-    if fam == "delta_kernel":
-        return n * e + 4 * n, 4 * r
-    raise KeyError(fam)
+    return n * e + 4 * n, 4 * r
 
 
 def kernel_model(wl: str, fam: str) -> dict:
@@ -383,12 +401,13 @@ def kernel_model(wl: str, fam: str) -> dict:
     N, d, e, heads = w["T"], w["hd"], w["e"], w["B"] * w["H"]
     nd = N * d
     comp_r, wr = compulsory_bytes(fam, w["B"], w["H"], N, d, e, w["fused_d"])
-    if fam in ("fwd32_kernel", "fwd_kernel"):
+    st = stage_of(fam)
+    if st == "fwd":
         req_r = nd * e + 2 * d * e * prefix_keys(N, *w["fwd"])
-    elif fam in ("dq32_kernel", "dq_kernel"):
+    elif st == "dq":
         extra = 4 * nd + 4 * N if w["fused_d"] else 8 * N  # O and L (D computed) or L and D
         req_r = 2 * nd * e + extra + 2 * d * e * prefix_keys(N, *w["dq"])
-    elif fam in ("dkv32_kernel", "dkv_kernel"):
+    elif st == "dkv":
         req_r = 2 * nd * e + (2 * d * e + 8) * suffix_rows(N, *w["dkv"])
     else:  # delta_kernel
         req_r = 4 * nd + nd * e
@@ -403,6 +422,8 @@ def workload_of(kernel: str) -> str | None:
     args = [x.strip() for x in s.split("<", 1)[1].rstrip(">").split(",")]
     if args[0] == "float":
         return "C2"
+    if s.split("<")[0] in ("fwd64_kernel", "dkv64_kernel"):  # hd 64 by construction
+        return "C3" if args[0] == "bf16_t" else None
     hd = args[1] if args[0] in ("bf16_t", "f16_t") else args[0]
     if args[0] == "f16_t":
         return None
@@ -560,15 +581,22 @@ def configs_report(log_path, out_md) -> None:
     for r in recs:
         t = r["times"]
         cell = lambda k: f"{t[k]['median_ms']:.4f} ({t[k]['min_ms']:.4f})"
-        err = max(r["parity"]["max_abs_err"].values())
+        errs = r["parity"]["max_abs_err"]
+        graded = r["parity"].get("graded", list(errs))
+        err = max(errs[n] for n in graded)
+        rest = [n for n in errs if n not in graded]
+        note = (f" ({', '.join(graded)}; {', '.join(rest)} not graded: {max(errs[n] for n in rest):.2e})"
+                if rest else "")
         lines.append(f"| {r['config']} | {r['workload']} | {r['B']} {r['H']} {r['T']} {r['hd']} | {r['dtype']} | "
                      f"{'yes' if r['causal'] else 'no'} | {r['precision']} | {r['counted_gflop']:.4g} | {cell('fwd')} | "
                      f"{cell('bwd')} | {cell('total')} | {r['tflops']:.2f} | {100 * r['frac_of_peak']:.2f} | "
-                     f"{err:.2e} / {r['parity']['tol']:.0e} {'ok' if r['parity']['ok'] else 'FAIL'} | "
+                     f"{err:.2e} / {r['parity']['tol']:.0e} {'ok' if r['parity']['ok'] else 'FAIL'}{note} | "
                      f"{r['oracle_s_per_head']:.4f} | {r['oracle_s_est']:.2f} |")
     lines += ["", "The tiny and ragged workloads are launch-bound (a few microseconds per kernel); they are "
               "correctness cases.  The precision column is the fa_precision code (0 default, 1 bf16 operands, 2 "
-              "split bf16 operands)."]
+              "split bf16 operands).  With P and dS rounded once to bfloat16 (precision 1) the long-context "
+              "gradients exceed the 2e-2 bar, so that row grades O and L only and reports the gradients' error; "
+              "the long-context workload runs with split operands (precision 2), which meet the bar."]
     Path(out_md).write_text("\n".join(lines) + "\n")
 
 
@@ -662,7 +690,8 @@ def grid_report(trace_db: str, asm_path: str, out_md: str, cus: int = 256) -> No
         seen.add(key)
         i += 1
         m = res.get(demangle.get(name.strip(), ""), None)
-        persistent = short_name(name).split("<")[0] in ("fwd32_kernel", "dq32_kernel", "dkv32_kernel")
+        persistent = short_name(name).split("<")[0] in ("fwd64_kernel", "dkv64_kernel", "fwd32_kernel", "dq32_kernel",
+                                                        "dkv32_kernel")
         if m:
             per = resident_workgroups(m["vgpr"], m["lds"], m["block"])
             slots = per * cus

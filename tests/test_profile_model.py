@@ -42,6 +42,13 @@ def test_bf16_forward_requests_match_closed_form():
 
 def test_kernel_names_map_to_workloads():
     assert P.workload_of("void fa::fwd32_kernel<fa::bf16_t, 64, true, 0, 2, 32, 2>(fa::FwdArgs)") == "C3"
+    assert P.workload_of("void fa::fwd64_kernel<fa::bf16_t, true, 0>(fa::FwdArgs)") == "C3"
+    assert P.workload_of("void fa::dkv64_kernel<fa::bf16_t, true, 1>(fa::BwdArgs)") == "C3"
+    assert P.workload_of("void fa::dkv64_kernel<fa::f16_t, true, 0>(fa::BwdArgs)") is None
+    assert P.family("void fa::dkv64_kernel<fa::bf16_t, true, 0>(fa::BwdArgs)") == "dkv64_kernel"
+    assert P.stage_of("dkv64_kernel") == "dkv" and P.stage_of("dq32_kernel") == "dq"
+    assert P.compulsory_bytes("fwd64_kernel", 64, 16, 1024, 64, 2, True) == \
+        P.compulsory_bytes("fwd32_kernel", 64, 16, 1024, 64, 2, True)
     assert P.workload_of("void fa::dkv32_kernel<fa::bf16_t, 128, true, 1, 4, 64>(fa::BwdArgs)") == "C4"
     assert P.workload_of("void fa::dq32_kernel<fa::f16_t, 64, true, 0, 4, 64, true>(fa::BwdArgs)") is None
     assert P.workload_of("void fa::dq_kernel<float, 64, true, 0, 4, 2, 32, false>(fa::BwdArgs)") == "C2"
