@@ -1,14 +1,14 @@
-// 16-bit (bfloat16 or IEEE half) dK/dV kernel for hd 64.
-//
-// Same algorithm, tiles and results as dkv32_kernel<TIn, 64, ..., NW = 4,
-// BQ = 64> ("Flash Attention 2 -- backward pass notes", section "dK/dV kernel
-// (one workgroup per K tile)"): four waves own 32 keys each of a 128-key
-// tile, with K and V fragments in registers; query blocks of 64 rows stream
-// past; per 32-row tile S^T and dP^T (stage A), P = exp2(S c - L log2 e) and
+// 16-bit (bfloat16 or IEEE half) dK/dV kernel for hd 64 ("Flash Attention 2
+// -- backward pass notes", section "The math (FA2 backward with recompute)"
+// and option 3 of "Why the WGSL kernel isn't shipped this turn": one owner per
+// key tile, no atomics).  Four waves own 32 keys each of a 128-key tile, with
+// K and V fragments in registers; query blocks of 64 rows stream past; per
+// 32-row tile S^T and dP^T (stage A), P = exp2(S c - L log2 e) and
 // dS = P (dP - D) (stage B), dV += P^T dO and dK += dS^T Q (stage C); dK is
-// scaled once at the end.
+// scaled once at the end.  Tiles wholly above a wave's first key are skipped
+// and the diagonal ones masked element-wise.
 //
-// What differs is the data movement.  Each workgroup walks one stream of
+// Data movement: each workgroup walks one stream of
 // equally sized LDS "positions": per work item its K tile, its V tile, then
 // its query blocks (Q and dO rows with their L and D).  Positions are filled
 // by direct global-to-LDS copies from a wave-uniform base plus fixed per-lane

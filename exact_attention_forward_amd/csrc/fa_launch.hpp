@@ -36,33 +36,28 @@ struct TileCfg;
 #ifndef FA_DQ_BC64
 #define FA_DQ_BC64 64
 #endif
-#ifndef FA_DKV_BQ64
-#define FA_DKV_BQ64 64
-#endif
 // hd 128: 32-key blocks in the forward and dQ kernels fit two waves per SIMD
-// (forward 217-231 VGPRs, dQ without fused D 232-235).  The 32x32 dK/dV
-// kernel cannot (236 spills at 256), so 16-bit hd 128 dK/dV, and dQ without
-// the causal mask, run the 16x16 kernels (see run_dq, run_dkv).
+// (forward 217-231 VGPRs, dQ without fused D 232-235).  A 32x32 dK/dV kernel
+// cannot (236 spills at 256), so 16-bit hd 128 dK/dV, and dQ without the
+// causal mask, run the 16x16 kernels (see run_dq, run_dkv); 16-bit hd 64 dK/dV
+// runs dkv64_kernel.
 #ifndef FA_FWD_BC128
 #define FA_FWD_BC128 32
 #endif
 #ifndef FA_DQ_BC128
 #define FA_DQ_BC128 32
 #endif
-#ifndef FA_DKV_BQ128
-#define FA_DKV_BQ128 64
-#endif
 #ifndef FA_NW64
 #define FA_NW64 4
 #endif
 // FWD_MS: 32-row sub-tiles per wave in the forward (rows per workgroup = 32 NW MS).
-// (DKV_BQ at hd 128 only matters to the 32x32 kernel, which hd 128 no longer uses.)
+// The 32x32 forward serves hd 128 and the split-key forward; hd 64's plain
+// forward is fwd64_kernel.
 template <int HD>
 struct TileCfg32 {
   static constexpr int FWD_NW = HD <= 64 ? FA_FWD_NW64 : 4, FWD_BC = HD <= 64 ? FA_FWD_BC64 : FA_FWD_BC128;
   static constexpr int FWD_MS = HD <= 64 ? FA_FWD_MS64 : 1;
   static constexpr int DQ_NW = HD <= 64 ? FA_NW64 : 4, DQ_BC = HD <= 64 ? FA_DQ_BC64 : FA_DQ_BC128;
-  static constexpr int DKV_NW = HD <= 64 ? FA_NW64 : 4, DKV_BQ = HD <= 64 ? FA_DKV_BQ64 : FA_DKV_BQ128;
 };
 
 template <int HD>
@@ -224,12 +219,6 @@ int run_dkv(const BwdArgs& a, hipStream_t s) {
     auto* k = &dkv64_kernel<TIn, CAUSAL, PREC>;
     const long items = (long)((a.T + 127) / 128) * a.B * a.H;
     hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, 256, items)), dim3(256), 0, s, a);
-    return launch_status();
-  } else if constexpr (is_16bit<TIn> && HD <= 64) {
-    using C = TileCfg32<HD>;
-    auto* k = &dkv32_kernel<TIn, HD, CAUSAL, PREC, C::DKV_NW, C::DKV_BQ>;
-    const long items = (long)((a.T + C::DKV_NW * 32 - 1) / (C::DKV_NW * 32)) * a.B * a.H;
-    hipLaunchKernelGGL(k, dim3((unsigned)persistent_grid(k, C::DKV_NW * 64, items)), dim3(C::DKV_NW * 64), 0, s, a);
     return launch_status();
   } else {
     using C = TileCfg<TIn, HD>;
