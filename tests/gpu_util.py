@@ -53,6 +53,18 @@ def head_errors(case: I.Case, out: dict, b: int, h: int) -> dict:
     return err
 
 
+def heads_errors(case: I.Case, out: dict, heads) -> dict:
+    """Max abs error over the given (b, h) heads, with each output copied to the host once."""
+    host = {n: t.cpu().numpy() for n, t in out.items()}
+    worst = {}
+    for b, h in heads:
+        ref = oracle_head(case, b, h)
+        for n in ("O", "L", "dQ", "dK", "dV", "D"):
+            g = host[n][b, h] if n in ("L", "D") else host[n][b, :, h]
+            worst[n] = max(worst.get(n, 0.0), float(np.abs(g.astype(np.float64) - ref[n]).max()))
+    return worst
+
+
 def full_errors(case: I.Case, out: dict) -> dict:
     """Max abs error over every head (for small cases)."""
     worst = {}

@@ -1,9 +1,11 @@
 """GPU parity against the float64 oracle, through the C ABI (needs an MI355X).
 
-Small cases are compared element by element over every output; the
-full-size workloads are compared on sampled heads (every output element of
-those heads), with the same entry points and precision mode the bench times.
-Tolerances: max abs 2e-5 for float32 inputs, 2e-2 for bfloat16 inputs.
+Small cases are compared element by element over every output.  The
+GPT-2-medium workloads (B64 H16 T1024 hd64, float32 and bfloat16) are
+compared on every head, the long-context one on eight spread heads (every
+output element of those heads), with the same entry points and precision mode
+the bench times.  Tolerances: max abs 2e-5 for float32 inputs, 2e-2 for
+bfloat16 inputs.
 """
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ import torch
 import exact_attention_forward_amd as fa
 from exact_attention_forward_amd import inputs as I
 
-from gpu_util import BF16_TOL, F32_TOL, assert_within, full_errors, head_errors, run_case
+from gpu_util import BF16_TOL, F32_TOL, assert_within, full_errors, head_errors, heads_errors, run_case
 
 pytestmark = pytest.mark.gpu
 
@@ -88,28 +90,27 @@ def gpt2m_bf16():
     return I.gpt2m_case(I.BF16)
 
 
-SAMPLE_HEADS = [(0, 0), (63, 15), (17, 5), (40, 11)]
-
 
 def check_sampled(case, prec, tol, heads):
     out = run_case(case, prec)
     for n, t in out.items():
         assert bool(torch.isfinite(t).all()), f"{n} has unwritten or non-finite elements"
-    worst = {}
-    for b, h in heads:
-        for n, e in head_errors(case, out, b, h).items():
-            worst[n] = max(worst.get(n, 0.0), e)
+    worst = heads_errors(case, out, heads)
     show(case, prec, worst)
     assert_within(worst, tol, case.name)
     return out
 
 
-def test_gpt2m_f32_sampled(gpt2m_f32):
-    check_sampled(gpt2m_f32, fa.FA_PREC_DEFAULT, F32_TOL, SAMPLE_HEADS)
+def all_heads(case):
+    return [(b, h) for b in range(case.B) for h in range(case.H)]
 
 
-def test_gpt2m_bf16_sampled(gpt2m_bf16):
-    check_sampled(gpt2m_bf16, fa.FA_PREC_BF16, BF16_TOL, SAMPLE_HEADS)
+def test_gpt2m_f32_all_heads(gpt2m_f32):
+    check_sampled(gpt2m_f32, fa.FA_PREC_DEFAULT, F32_TOL, all_heads(gpt2m_f32))
+
+
+def test_gpt2m_bf16_all_heads(gpt2m_bf16):
+    check_sampled(gpt2m_bf16, fa.FA_PREC_BF16, BF16_TOL, all_heads(gpt2m_bf16))
 
 
 # Ragged T with enough (query or key tile, head) items that every persistent
@@ -130,7 +131,8 @@ def test_bf16_ragged_multi_item_sampled(shape, causal):
 
 def test_long_bf16_split_sampled():
     c = I.long_case()
-    check_sampled(c, fa.FA_PREC_BF16X2, BF16_TOL, [(0, 0), (3, 15)])
+    heads = [(0, 0), (0, 7), (1, 3), (1, 12), (2, 5), (2, 14), (3, 9), (3, 15)]
+    check_sampled(c, fa.FA_PREC_BF16X2, BF16_TOL, heads)
 
 
 # -- properties --------------------------------------------------------------------
