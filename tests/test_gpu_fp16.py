@@ -26,7 +26,7 @@ from gpu_util import BF16_TOL, assert_within, full_errors, head_errors, run_case
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(1, 2, 300, 64), (2, 1, 129, 128), (1, 1, 1024, 64), (1, 3, 33, 64)]
+SHAPES = [(1, 2, 300, 64), (2, 1, 129, 128), (1, 1, 1024, 64), (1, 3, 33, 64), (1, 2, 191, 64), (2, 1, 130, 64)]
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -54,7 +54,12 @@ def test_f32_edges(shape, causal):
     assert_within(err, F32_TOL, c.name)
 
 
-BF16_EDGES = [(1, 1, 1, 64), (1, 2, 31, 64), (2, 1, 257, 64), (1, 2, 300, 128), (1, 1, 65, 128), (1, 1, 700, 64)]
+# hd 64 lengths around the streamed kernels' tiles (32-key blocks and 128-row
+# query tiles in the forward; 128-key tiles and 64-row query blocks in dK/dV):
+# one partial block, a query tile of two rows, one row short of three query
+# blocks, whole blocks only, and a diagonal that ends inside a partial block.
+BF16_EDGES = [(1, 1, 1, 64), (1, 2, 31, 64), (2, 1, 257, 64), (1, 2, 300, 128), (1, 1, 65, 128), (1, 1, 700, 64),
+              (1, 3, 100, 64), (2, 2, 130, 64), (1, 1, 191, 64), (3, 1, 64, 64), (1, 2, 384, 64), (1, 1, 449, 64)]
 
 
 @pytest.mark.parametrize("shape", BF16_EDGES, ids=lambda s: "B{}H{}T{}hd{}".format(*s))
