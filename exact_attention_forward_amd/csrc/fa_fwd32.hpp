@@ -66,6 +66,7 @@ __device__ __forceinline__ void sum8(f16x8 v, unsigned one2, float& acc0, float&
 
 // Exponent headroom (base 2) before the reference max is raised.
 constexpr float kRescaleSlack = 8.f;
+constexpr float kSlackWeight = 256.f;  // 2^kRescaleSlack: the largest P the reference rule allows
 
 // Max of the 16 elements of a C tile, as a shallow tree.
 __device__ __forceinline__ float tile_max(const f32x16& x) {

@@ -6,7 +6,8 @@
 // 32-row sub-tiles; S^T = K Q^T with Q in registers, the online softmax with
 // a lazily raised reference max, O^T += V^T P^T with P from the S registers;
 // O / l and L = m + ln l at the end.  The results are bitwise those of
-// fwd32_kernel; what differs is the instruction stream.
+// fwd32_kernel (up to a block whose row-sum increment lies within rounding of
+// 2^slack, below); what differs is the instruction stream.
 //
 // At two waves per SIMD the forward is bound by vector-ALU issue, and each
 // wave's own stream is a chain (scores -> max -> exp -> P V) that the other
@@ -22,6 +23,9 @@
 //    scores of block j + 1 are issued in the same straight-line region as
 //    the exponentials and P V products of block j, with two score buffers
 //    alternating (no register copies between steps).
+//  - With single-rounded P, a pipelined block takes no row max: the row-sum
+//    increments show whether the reference would have been raised, and only
+//    then is the block redone with the max.
 //  - The diagonal and ragged blocks keep the per-block code of fwd32_kernel
 //    with compile-time mask states.
 #pragma once
@@ -268,14 +272,26 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int u = 0; u < MS; ++u) s[u] = mma32(kop[ks], qf[u][ks], s[u]);
     };
+    // With single-rounded P (PREC 0) a pipelined block skips the row max:
+    // its exponentials use the current reference, and the increments of the
+    // row sums decide afterwards.  If every P of the block is below 2^slack
+    // (each increment below it), the reference rule would not have raised the
+    // reference, so the result is the one the max would have given; otherwise
+    // (rare once a row's first block set the reference) the sums are restored
+    // and the sub-tile is redone with the max, its scores recomputed from the
+    // K block still in LDS.  The first pipelined block takes the max before
+    // the loop.
+    constexpr bool SKIP_MAX = PREC == 0;
     auto pipe_step = [&](f32x16* sc, f32x16* sn, auto has_next) {
       constexpr bool NX = decltype(has_next)::value;
       // block pos (V) and, with NX, block pos + 1 (K) complete and visible
       wait_vm(CPB * min(LOOK - 1, issued - 1 - (NX ? pos + 1 : pos)));
       __syncthreads();
       if (dw >= 0) issue();
+      if (!SKIP_MAX) {
 #pragma unroll
-      for (int u = 0; u < MS; ++u) softmax_max(u, sc[u], 0, std::false_type{});
+        for (int u = 0; u < MS; ++u) softmax_max(u, sc[u], 0, std::false_type{});
+      }
       const int sl = pos % NSLOT;
       V8 vop[2][NDT];
 #pragma unroll
@@ -286,7 +302,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int u = 0; u < MS; ++u) {
         V8 pk[2], pl[2];
+        const float l0 = ls0[u], l1 = ls1[u];
         softmax_exp(u, sc[u], pk, pl);
+        if (SKIP_MAX && __any((ls0[u] - l0) + (ls1[u] - l1) >= kSlackWeight)) {
+          ls0[u] = l0;
+          ls1[u] = l1;
+          f32x16 s = zero16();
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) s = mma32(ld_k(sl, ks), qf[u][ks], s);
+          softmax_max(u, s, 0, std::false_type{});
+          softmax_exp(u, s, pk, pl);
+        }
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -305,6 +331,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // two score buffers alternate, so no copies between steps
       f32x16 sa[MS], sb[MS];
       scores(pos % NSLOT, sa);
+      if (SKIP_MAX) {
+#pragma unroll
+        for (int u = 0; u < MS; ++u) softmax_max(u, sa[u], 0, std::false_type{});
+      }
       int kb = 0;
       for (; kb + 2 < nfull; kb += 2) {
         pipe_step(sa, sb, std::true_type{});

@@ -708,7 +708,8 @@ def grid_report(trace_db: str, asm_path: str, out_md: str, cus: int = 256) -> No
             "    rocprofv3 --kernel-trace --stats -d $OUT/prof_grid -o grid -- python3 bench.py --counters "
             "--workloads C4,C3",
             "    hipcc -O3 -std=c++17 --offload-arch=gfx950 -Xclang -target-feature -Xclang -packed-fp32-ops "
-            "--cuda-device-only -S exact_attention_forward_amd/csrc/fa_inst_bf16.hip -o $OUT/bf16.s",
+            "-Xarch_device -fno-honor-nans --cuda-device-only -S exact_attention_forward_amd/csrc/fa_inst_bf16.hip "
+            "-o $OUT/bf16.s",
             "    python -m exact_attention_forward_amd.profile grid $OUT/prof_grid/grid_results.db $OUT/bf16.s "
             "<this file>", "",
             "The counter run steps B4 H16 T8192 hd128 (split operands) and then B64 H16 T1024 hd64 (bf16 operands), "

@@ -164,3 +164,32 @@ def test_forward_auto_split_under_graph_capture():
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(o, eo) and torch.equal(lse, el), f"warm={warm}"
+
+
+@pytest.mark.parametrize("growing", [False, True], ids=["plain_keys", "growing_keys"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_streamed_forward_is_the_tile_kernel_bit_for_bit(causal, growing):
+    # At hd 64 the plain forward (one split, no workspace) runs the streamed
+    # kernel, which skips the row max of a pipelined block and redoes the
+    # block with it only when a row-sum increment shows a weight of 2^slack or
+    # more; the split forward with one split runs the per-block tile kernel,
+    # which takes every block's max, and a merge that returns its one partial
+    # unchanged.  Both must give the same bits.  With the keys of the second
+    # half scaled by 6, later blocks' scores exceed each row's reference by far
+    # more than the slack, so the redo path runs (and raises the reference).
+    B, H, T, hd = 2, 3, 700, 64
+    c = I.make_case("streamed_vs_tile", B, H, T, hd, I.BF16, causal, 31)
+    if growing:
+        k = I.bf16_bits_to_f32(c.k).copy()
+        k[:, T // 2:] *= 6.0
+        c.k = I.f32_to_bf16_bits(k).reshape(c.k.shape)
+    q, k, v = (to_device(c, x) for x in ("q", "k", "v"))
+    o1 = torch.full((B, T, H, hd), float("nan"), device="cuda")
+    l1 = torch.full((B, H, T), float("nan"), device="cuda")
+    fa.check(fa.fa_forward_splitkv(q, k, v, o1, l1, None, B, H, T, hd, c.scale, int(causal), 1, fa.FA_BF16,
+                                   fa.FA_PREC_BF16, None))
+    o2, l2 = run_split(c, 1, fa.FA_PREC_BF16)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    err = oracle_errors(c, o1, l1)
+    print(f"[streamed vs tile] causal={causal} growing={growing} {err}", flush=True)
+    assert err["O"] <= BF16_TOL and err["L"] <= BF16_TOL, err
