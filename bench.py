@@ -43,6 +43,11 @@ kernels against the float64 reference with the lesson's error bound is checked
 by tests/test_gpu_lab.py.  ``--lab --counters`` instead runs the calibration
 copy and then each (N, d, kind) once, for rocprofv3 --pmc.
 
+``--ramp N`` times each of the first N steps of the bench workload from the
+first call of the process (HIP events between consecutive steps), then 20
+steps after 200 ms of idle, and the mean over the window that --warmup W
+--steps K would time: how the step time settles while the clock does.
+
 ``--split`` times the split-key forward against the plain forward on causal
 workloads with few (batch, head) pairs and long sequences (B1 H4 T8192 hd128,
 B1 H8 T16384 hd64, B1 H2 T32768 hd128 in bfloat16, B1 H4 T8192 hd64 in
@@ -133,6 +138,8 @@ def parse():
     ap.add_argument("--configs", action="store_true", help="time and check every workload, not only the bench one")
     ap.add_argument("--split", action="store_true",
                     help="split-key forward against the plain forward on few-head long-sequence workloads")
+    ap.add_argument("--ramp", type=int, default=0, metavar="N",
+                    help="time each of the first N steps of a fresh process, and 20 more after 200 ms idle")
     return ap.parse_args()
 
 
@@ -183,6 +190,9 @@ def main() -> int:
         fa.check(fa.fa_backward_dkv(q, k, v, lse, do, delta, dk, dv, B, H, T, hd, sc, 1, dt, prec, stream))
         if ev is not None:
             ev[3].record(stream)
+
+    if args.ramp:
+        return ramp(args.ramp, step, stream, args)
 
     if args.counters:
         x = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
@@ -246,6 +256,35 @@ def main() -> int:
         rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(case, dict(O=o, L=lse, dQ=dq, dK=dk, dV=dv),
                                                                  args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+    return 0
+
+
+def ramp(n: int, step, stream, args) -> int:
+    """Per-step times (HIP events between consecutive steps) from the first call of a fresh process.
+
+    Also reports the mean over the window a run with --warmup W --steps K would time, and 20 steps
+    after 200 ms of idle, so that the settling of the clock under this load can be read off.
+    """
+    import torch
+
+    def timed(count):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(count + 1)]
+        ev[0].record(stream)
+        for i in range(count):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return [round(ev[i].elapsed_time(ev[i + 1]), 4) for i in range(count)]
+
+    torch.cuda.synchronize()
+    first = timed(n)
+    time.sleep(0.2)
+    again = timed(20)
+    w, k = args.warmup, args.steps
+    window = first[w:w + k]
+    print(json.dumps({"ramp_steps_ms": first, "after_idle_200ms_ms": again, "warmup": w, "steps": k,
+                      "window_mean_ms": round(sum(window) / len(window), 4) if len(window) == k else None,
+                      "last_20_mean_ms": round(sum(first[-20:]) / 20, 4) if n >= 20 else None}), flush=True)
     return 0
 
 
