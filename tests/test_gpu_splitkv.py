@@ -24,7 +24,7 @@ def run_split(c, nsplit, prec=fa.FA_PREC_DEFAULT):
     o = torch.full((B, T, H, hd), float("nan"), device="cuda")
     lse = torch.full((B, H, T), float("nan"), device="cuda")
     ws = torch.full((nsplit * (B * T * H * hd + B * H * T),), float("nan"), device="cuda")
-    dt = fa.FA_BF16 if c.dtype == I.BF16 else fa.FA_F32
+    dt = {I.BF16: fa.FA_BF16, I.F16: fa.FA_F16}.get(c.dtype, fa.FA_F32)
     fa.check(fa.fa_forward_splitkv(q, k, v, o, lse, ws, B, H, T, hd, c.scale, int(c.causal), nsplit, dt, prec, None))
     torch.cuda.synchronize()
     return o, lse
@@ -166,9 +166,10 @@ def test_forward_auto_split_under_graph_capture():
             assert torch.equal(o, eo) and torch.equal(lse, el), f"warm={warm}"
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("growing", [False, True], ids=["plain_keys", "growing_keys"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_streamed_forward_is_the_tile_kernel_bit_for_bit(causal, growing):
+def test_streamed_forward_is_the_tile_kernel_bit_for_bit(causal, growing, dt):
     # At hd 64 the plain forward (one split, no workspace) runs the streamed
     # kernel, which skips the row max of a pipelined block and redoes the
     # block with it only when a row-sum increment shows a weight of 2^slack or
@@ -178,18 +179,19 @@ def test_streamed_forward_is_the_tile_kernel_bit_for_bit(causal, growing):
     # half scaled by 6, later blocks' scores exceed each row's reference by far
     # more than the slack, so the redo path runs (and raises the reference).
     B, H, T, hd = 2, 3, 700, 64
-    c = I.make_case("streamed_vs_tile", B, H, T, hd, I.BF16, causal, 31)
+    bf = dt == "bf16"
+    c = I.make_case("streamed_vs_tile", B, H, T, hd, I.BF16 if bf else I.F16, causal, 31)
     if growing:
-        k = I.bf16_bits_to_f32(c.k).copy()
+        k = I.bf16_bits_to_f32(c.k).copy() if bf else c.k.view(np.float16).astype(np.float32)
         k[:, T // 2:] *= 6.0
-        c.k = I.f32_to_bf16_bits(k).reshape(c.k.shape)
+        c.k = I.f32_to_bf16_bits(k).reshape(c.k.shape) if bf else k.astype(np.float16).view(np.uint16)
     q, k, v = (to_device(c, x) for x in ("q", "k", "v"))
     o1 = torch.full((B, T, H, hd), float("nan"), device="cuda")
     l1 = torch.full((B, H, T), float("nan"), device="cuda")
-    fa.check(fa.fa_forward_splitkv(q, k, v, o1, l1, None, B, H, T, hd, c.scale, int(causal), 1, fa.FA_BF16,
-                                   fa.FA_PREC_BF16, None))
-    o2, l2 = run_split(c, 1, fa.FA_PREC_BF16)
+    code, prec = (fa.FA_BF16, fa.FA_PREC_BF16) if bf else (fa.FA_F16, fa.FA_PREC_DEFAULT)
+    fa.check(fa.fa_forward_splitkv(q, k, v, o1, l1, None, B, H, T, hd, c.scale, int(causal), 1, code, prec, None))
+    o2, l2 = run_split(c, 1, prec)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     err = oracle_errors(c, o1, l1)
-    print(f"[streamed vs tile] causal={causal} growing={growing} {err}", flush=True)
+    print(f"[streamed vs tile] {dt} causal={causal} growing={growing} {err}", flush=True)
     assert err["O"] <= BF16_TOL and err["L"] <= BF16_TOL, err
