@@ -30,6 +30,13 @@
 
 namespace fa {
 
+// -x of eight 16-bit floats (bfloat16 or binary16): the sign bits flipped.
+template <typename V>
+__device__ __forceinline__ V neg16(V x) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(V, __builtin_bit_cast(u32x4_t, x) ^ 0x80008000u);
+}
+
 template <typename TIn, bool CAUSAL, int PREC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv64_kernel(BwdArgs a) {
   constexpr int HD = 64, NW = 4, NT = NW * 64;
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       kf[ks] = ld_row(slot_base(pos), 0, 32 * wave, ks);
-      vf[ks] = ld_row(slot_base(pos + 1), 0, 32 * wave, ks);
+      vf[ks] = neg16(ld_row(slot_base(pos + 1), 0, 32 * wave, ks));
     }
     pos += 2;
 
@@ -256,8 +263,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // address sb, first row q0): A = the S and dP products, B = P and dS in
     // registers, C = the dV and dK products.  MASK: causal diagonal.
     auto stage_a = [&](unsigned sb, int it, f32x16& sa, f32x16& da) __attribute__((always_inline)) {
+      typedef __attribute__((address_space(3))) f32x4 lds_f4;
       sa = zero16();
-      da = zero16();
+      // The second product starts from D of its rows and accumulates dO (-V)^T
+      // (the V fragments are held negated), giving D - dP: stage B forms
+      // dS = P (dP - D) = -P (D - dP) with one multiply.  D is read here,
+      // before the barrier of the block for the pipelined blocks' first tile;
+      // unlike L it is never rewritten in LDS.
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const f32x4 d = *(const lds_f4*)(uintptr_t)(sb + LOFF + 4 * (BQ + 32 * it + 8 * bb + 4 * h));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) da[4 * bb + r] = d[r];
+      }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         sa = mma32(ld_row(sb, 0, 32 * it, ks), kf[ks], sa);
@@ -270,21 +288,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       constexpr bool MASK = decltype(masked)::value;
       const unsigned sb = slot_base(sl);
       const float* cL = reinterpret_cast<const float*>(&ring[sl][LOFF]);
-      const float* cD = cL + BQ;
       const int lim = lo - (q0 + 32 * it);
       V8 bp[2], bs[2], bpl[2], bsl[2];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const int rr = 32 * it + 8 * bb + 4 * h;
         const f32x4 lv = *reinterpret_cast<const f32x4*>(&cL[rr]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&cD[rr]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = 4 * bb + r;
           float p = fast_exp2(fmaf(sc[e], c2, -lv[r]));
           if (MASK && CAUSAL && 8 * bb + r < lim) p = 0.f;
           sc[e] = p;
-          dc[e] = p * (dc[e] - d4[r]);
+          dc[e] = -(p * dc[e]);  // dc held D - dP
         }
       }
 #pragma unroll
