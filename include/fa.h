@@ -20,9 +20,11 @@
  * Scale.    Scores are scale * <q_i, k_j>; scale must be finite and > 0
  *           (1/sqrt(hd) in the usual case).
  * Memory.   Every pointer is a device pointer allocated by the caller,
- *           16-byte aligned.  The library never allocates, frees or
- *           synchronises; it only enqueues kernels on `stream` (a hipStream_t,
- *           NULL for the default stream), in order, and returns.  Inputs are
+ *           16-byte aligned.  The library only enqueues kernels on `stream`
+ *           (a hipStream_t, NULL for the default stream), in order, and
+ *           returns; it allocates, frees or synchronises in one case only:
+ *           fa_forward's own key split (its workspace, described there).
+ *           fa_backward_nows uses a static device array instead.  Inputs are
  *           read-only.  Outputs are fully overwritten (no pre-zeroing, nothing
  *           accumulates).  Outputs must not overlap each other or any input.
  * Errors.   0 on success, a negative FA_ERR_* code otherwise.  All argument
