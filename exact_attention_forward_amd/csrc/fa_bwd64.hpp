@@ -267,9 +267,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       sa = zero16();
       // The second product starts from D of its rows and accumulates dO (-V)^T
       // (the V fragments are held negated), giving D - dP: stage B forms
-      // dS = P (dP - D) = -P (D - dP) with one multiply.  D is read here,
-      // before the barrier of the block for the pipelined blocks' first tile;
-      // unlike L it is never rewritten in LDS.
+      // dS = P (dP - D) = -P (D - dP) with one multiply.  For the first tile
+      // of the next block (pipelined order) this read comes before that
+      // block's barrier: its copies completed and became visible at the
+      // barrier before, and D, unlike L, is never rewritten in LDS.
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const f32x4 d = *(const lds_f4*)(uintptr_t)(sb + LOFF + 4 * (BQ + 32 * it + 8 * bb + 4 * h));
