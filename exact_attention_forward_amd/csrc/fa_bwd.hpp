@@ -308,7 +308,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       kf[mr][ks] = M::ld_row_global(K, rs, j, T, ks * M::KS, lg);
-      vf[mr][ks] = M::ld_row_global(V, rs, j, T, ks * M::KS, lg);
+      vf[mr][ks] = neg_frag(M::ld_row_global(V, rs, j, T, ks * M::KS, lg));  // held negated: see dp below
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) dk[dt][mr] = dv[dt][mr] = zero4();
@@ -357,9 +357,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         f32x4 s[MR][TPC], dp[MR][TPC];
 #pragma unroll
         for (int t = 0; t < TPC; ++t) {
-#pragma unroll
-          for (int mr = 0; mr < MR; ++mr) s[mr][t] = dp[mr][t] = zero4();
           const int ir = ch * M::CH + 16 * t;
+          // dp starts from D of its rows and accumulates dO (-V)^T, giving
+          // D - dP, so dS = P (dP - D) below takes one multiply
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[buf][ir + 4 * lg]);
+#pragma unroll
+          for (int mr = 0; mr < MR; ++mr) {
+            s[mr][t] = zero4();
+            dp[mr][t] = d4;
+          }
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const frag qa = M::ld_row(cQ, LD, ir, ks * M::KS, li, lg);
@@ -376,7 +382,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int t = 0; t < TPC; ++t) {
           const int ir = ch * M::CH + 16 * t + 4 * lg;
           const f32x4 lv = *reinterpret_cast<const f32x4*>(&sL[buf][ir]);
-          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&sD[buf][ir]);
 #pragma unroll
           for (int mr = 0; mr < MR; ++mr) {
             const int j = c0 + 16 * mr + li;
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
               float p = fast_exp2(fmaf(s[mr][t][r], c2, -lv[r]));
               if (need_mask && (q0 + ir + r < j)) p = 0.f;
               s[mr][t][r] = p;
-              dp[mr][t][r] = p * (dp[mr][t][r] - dv4[r]);
+              dp[mr][t][r] = -(p * dp[mr][t][r]);  // dp held D - dP
             }
           }
         }

@@ -30,13 +30,6 @@
 
 namespace fa {
 
-// -x of eight 16-bit floats (bfloat16 or binary16): the sign bits flipped.
-template <typename V>
-__device__ __forceinline__ V neg16(V x) {
-  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-  return __builtin_bit_cast(V, __builtin_bit_cast(u32x4_t, x) ^ 0x80008000u);
-}
-
 template <typename TIn, bool CAUSAL, int PREC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv64_kernel(BwdArgs a) {
   constexpr int HD = 64, NW = 4, NT = NW * 64;
@@ -251,7 +244,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       kf[ks] = ld_row(slot_base(pos), 0, 32 * wave, ks);
-      vf[ks] = neg16(ld_row(slot_base(pos + 1), 0, 32 * wave, ks));
+      vf[ks] = neg_frag(ld_row(slot_base(pos + 1), 0, 32 * wave, ks));
     }
     pos += 2;
 

@@ -40,6 +40,16 @@ struct f16_t {
 };
 typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 
+// -x of an MFMA operand fragment: a float, or eight 16-bit floats (bfloat16
+// or binary16, sign bits flipped).
+__device__ __forceinline__ float neg_frag(float x) { return -x; }
+__device__ __forceinline__ bf16x8 neg_frag(bf16x8 x) {
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
+}
+__device__ __forceinline__ f16x8 neg_frag(f16x8 x) {
+  return __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, x) ^ 0x80008000u);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
