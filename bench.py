@@ -123,6 +123,21 @@ def measured_traffic(stage: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def hbm_summary(per_ms: dict, ms_step: float):
+    """HBM bytes of one step (the counter record's bytes per launch of each kernel) against the step time
+    and each kernel's time, as a fraction of the 8 TB/s peak; None unless every kernel has a record
+    that matches the current kernel sources."""
+    got = {s: measured_traffic(s) for s in STAGES}
+    if any(b is None for b in got.values()):
+        return None
+    total = sum(got.values())
+    gbs = total / (ms_step * 1e-3) / 1e9
+    return {"bytes_per_step": total, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "kernels": {KERNEL_NAMES[s]: {"bytes": b, "achieved": round(b / (per_ms[s] * 1e-3) / 1e9, 1)}
+                        for s, b in got.items()}}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,7 +263,7 @@ def main() -> int:
         "config": {"workload": "causal attention fwd+bwd B64 H16 T1024 hd64 bf16 (P, dS bf16 operands)",
                    "B": B, "H": H, "T": T, "hd": hd, "causal": True, "precision": "FA_PREC_BF16"},
         "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "kernels": kernels,
+        "roofline": roofline, "hbm": hbm_summary(per, ms_step), "kernels": kernels,
         "device": torch.cuda.get_device_name(dev),
     }
 
