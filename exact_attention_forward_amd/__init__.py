@@ -3,8 +3,9 @@
 The computation lives in the HIP library ``libfa.so`` (C ABI: include/fa.h),
 built from ``csrc/`` by ``exact_attention_forward_amd.build``.  This package
 holds the ctypes binding (``fa_*``, same names and arguments as the C entry
-points), a torch convenience layer (``forward``, ``backward``; torch only
-provides memory and streams) and the seeded input generators (``inputs``).
+points), a torch convenience layer (``forward``, ``backward`` and the autograd
+operation ``attention``; torch only provides memory and streams) and the seeded
+input generators (``inputs``).
 """
 from ._binding import (FA_BF16, FA_F16, FA_ERR_ALIAS, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_LAUNCH, FA_ERR_TOO_LARGE, FA_ERR_UNSUPPORTED, FA_F32,
                        FA_OK, FA_PREC_BF16, FA_PREC_BF16X2, FA_PREC_DEFAULT, FaError, check, fa_backward,
@@ -13,7 +14,7 @@ from ._binding import (FA_BF16, FA_F16, FA_ERR_ALIAS, FA_ERR_ALIGN, FA_ERR_ARG, 
 
 
 def __getattr__(name):
-    if name in ("forward", "backward"):
+    if name in ("forward", "backward", "attention"):
         from . import api
 
         return getattr(api, name)

@@ -5,7 +5,8 @@ computation runs in the HIP library.  Inputs are contiguous [B, T, H, hd]
 device tensors of one dtype (float32, bfloat16 or float16) on one device;
 outputs are float32.  Every tensor argument is checked here, before the
 library is called: the C ABI sees only raw pointers and would read a tensor
-of another dtype or size out of bounds.
+of another dtype or size out of bounds.  ``attention`` wraps the two calls
+as one autograd operation.
 """
 from __future__ import annotations
 
@@ -99,3 +100,30 @@ def backward(q, k, v, o, lse, do, scale: float | None = None, causal: bool = Tru
     check(_b.fa_backward(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, T, hd, scale, causal, _dtype_code(q), prec,
                          stream))
     return dq, dk, dv, delta
+
+
+class _Attention(torch.autograd.Function):
+    """fa_forward in the forward pass, fa_backward in the backward pass (O and L saved between)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale, causal, prec):
+        o, lse = forward(q, k, v, scale, causal, prec)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.cfg = (scale, causal, prec)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        scale, causal, prec = ctx.cfg
+        # the library takes dO in the inputs' dtype
+        do = do.to(q.dtype).contiguous()
+        dq, dk, dv, _ = backward(q, k, v, o, lse, do, scale, causal, prec)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None
+
+
+def attention(q, k, v, scale: float | None = None, causal: bool = True, prec: int = FA_PREC_DEFAULT):
+    """O = softmax(mask(scale q k^T)) v as an autograd operation: returns o (float32 [B, T, H, hd]);
+    o.backward(dO) runs fa_backward with dO rounded to the inputs' dtype and leaves dq, dk, dv in
+    q.grad, k.grad, v.grad, rounded to the inputs' dtype."""
+    return _Attention.apply(q, k, v, scale, causal, prec)

@@ -74,3 +74,13 @@ def test_backward_checks_do_o_and_lse(stubbed):
 def test_device_tensors_required():
     with pytest.raises(ValueError):
         api.forward(*(t(1, 8, 2, 64) for _ in range(3)))
+
+
+def test_attention_runs_forward_then_backward_with_the_saved_outputs(stubbed):
+    q, k, v = (t(1, 8, 2, 64).requires_grad_() for _ in range(3))
+    o = api.attention(q, k, v)
+    assert stubbed == ["fwd"] and o.dtype == torch.float32 and o.requires_grad
+    o.backward(torch.ones_like(o))
+    assert stubbed == ["fwd", "bwd"]
+    for x in (q, k, v):
+        assert x.grad is not None and x.grad.dtype == torch.bfloat16 and x.grad.shape == x.shape
